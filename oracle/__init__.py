@@ -1,0 +1,139 @@
+"""Python face of the CPU oracle (``csa_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the library.  It shares no code with the
+HIP path.  ``build()`` compiles the C file with gcc (OpenMP, ``-ffp-contract=off``
+so that no multiply-add is fused); the shared object lives in ``oracle/_build``.
+
+All functions take a :class:`synth.Problem` (bf16 bit patterns, head-major q)
+and return numpy arrays.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "csa_oracle.c")
+_BUILD = os.path.join(_HERE, "_build")
+_SO = os.path.join(_BUILD, "libcsa_oracle.so")
+
+# x86-64-v3 (AVX2/FMA) keeps the object runnable on any recent host; the
+# contraction switch keeps every multiply and add separately rounded.
+CFLAGS = ["-O3", "-march=x86-64-v3", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+          "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra"]
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle; returns the path of the shared object."""
+    os.makedirs(_BUILD, exist_ok=True)
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        tmp = _SO + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_SO)
+    i64, f32, f64, vp = ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
+    lib.csa_oracle_scores_f32.argtypes = [i64] * 6 + [f32] + [vp] * 6 + [i64, vp, vp]
+    lib.csa_oracle_scores_f32.restype = None
+    lib.csa_oracle_scores_f64.argtypes = [i64] * 6 + [f64] + [vp] * 6 + [i64, vp, vp]
+    lib.csa_oracle_scores_f64.restype = None
+    lib.csa_oracle_valid.argtypes = [i64, i64, i64, vp, vp, vp, i64, vp, vp]
+    lib.csa_oracle_valid.restype = None
+    lib.csa_oracle_topk.argtypes = [i64, i64, i64, vp, vp]
+    lib.csa_oracle_topk.restype = None
+    lib.csa_oracle_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _rows_arg(P, rows):
+    if rows is None:
+        return P.B * P.S, None
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    if r.size and (r.min() < 0 or r.max() >= P.B * P.S):
+        raise ValueError("row id out of range")
+    return int(r.size), r
+
+
+def _check(P):
+    for name, arr, shape in (("q", P.q, (P.B, P.H, P.S, P.D)), ("k", P.k, (P.B, P.W, P.D)),
+                             ("w", P.w, (P.B, P.S, P.H))):
+        if tuple(arr.shape) != shape or arr.dtype != np.uint16:
+            raise ValueError(f"{name}: expected uint16 {shape}, got {arr.dtype} {arr.shape}")
+    if (P.q_seg is None) != (P.k_seg is None):
+        raise ValueError("q_seg and k_seg go together")
+    if P.m < 1:
+        raise ValueError("compress rate must be >= 1")
+
+
+def scores(P, rows: Optional[Sequence[int]] = None, precision: str = "f32") -> np.ndarray:
+    """Masked scores of the given rows (b*S+i), shape [n_rows, W]; -inf = masked."""
+    _check(P)
+    lib = _load()
+    n, r = _rows_arg(P, rows)
+    q, k, w = _c(P.q, np.uint16), _c(P.k, np.uint16), _c(P.w, np.uint16)
+    qo, qs, ks = _c(P.q_offset, np.int32), _c(P.q_seg, np.int32), _c(P.k_seg, np.int32)
+    args = (P.B, P.S, P.H, P.D, P.W, P.m)
+    if precision == "f32":
+        out = np.empty((n, P.W), dtype=np.float32)
+        lib.csa_oracle_scores_f32(*args, float(P.scale), _ptr(q), _ptr(k), _ptr(w), _ptr(qo),
+                                  _ptr(qs), _ptr(ks), n, _ptr(r), _ptr(out))
+    elif precision == "f64":
+        out = np.empty((n, P.W), dtype=np.float64)
+        lib.csa_oracle_scores_f64(*args, float(P.scale), _ptr(q), _ptr(k), _ptr(w), _ptr(qo),
+                                  _ptr(qs), _ptr(ks), n, _ptr(r), _ptr(out))
+    else:
+        raise ValueError(precision)
+    return out
+
+
+def valid(P, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Boolean candidate mask of the given rows, shape [n_rows, W]."""
+    lib = _load()
+    n, r = _rows_arg(P, rows)
+    out = np.empty((n, P.W), dtype=np.uint8)
+    lib.csa_oracle_valid(P.S, P.W, P.m, _ptr(_c(P.q_offset, np.int32)), _ptr(_c(P.q_seg, np.int32)),
+                         _ptr(_c(P.k_seg, np.int32)), n, _ptr(r), _ptr(out))
+    return out.astype(bool)
+
+
+def topk(score_rows: np.ndarray, top_k: int) -> np.ndarray:
+    """Top-k indices of each row of a [rows, W] float32 matrix (-inf/NaN never chosen)."""
+    s = np.ascontiguousarray(score_rows, dtype=np.float32)
+    if s.ndim != 2:
+        raise ValueError("expected [rows, W]")
+    if top_k < 1:
+        raise ValueError("top_k must be >= 1")
+    out = np.empty((s.shape[0], top_k), dtype=np.int32)
+    _load().csa_oracle_topk(s.shape[0], s.shape[1], top_k, _ptr(s), _ptr(out))
+    return out
+
+
+def select(P, rows: Optional[Sequence[int]] = None):
+    """(scores [n_rows, W] fp32, idx [n_rows, top_k] int32) of the given rows."""
+    s = scores(P, rows)
+    return s, topk(s, P.top_k)

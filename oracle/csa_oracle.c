@@ -1,0 +1,213 @@
+/*
+ * csa_oracle.c -- plain CPU oracle for the CSA indexer score and top-k path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this code.  It shares nothing with
+ * the HIP library: no headers, no helpers, no tables.
+ *
+ * What it computes (one query row i of batch b, compressed entry j):
+ *
+ *   logit[h]   = sum_t q[b,h,i,t] * k[b,j,t]            bf16 inputs, fp32 sums
+ *   score[i,j] = scale * sum_h w[b,i,h] * ReLU(logit[h])  fp32
+ *
+ * following the fused StreamIndex score (MaxText PR #5079 "Add StreamIndex
+ * Kernel for CSA": head-major q [B,H,S,D], compressed keys [B,W,D], weights
+ * [B,S,H], scores [B,S,W]; bf16 einsums with float32 accumulation per the
+ * commit that chunks the head accumulation).  Masks follow MaxText PR #4915
+ * ("DSV4: Add indexer_save_selection and indexer_sharded_topk", inline review
+ * of the indexer's future mask): entry j is a future entry of row i when
+ * j >= causal_threshold(i); with absolute row position p = q_offset[b] + i,
+ * causal_threshold = floor((p + 1) / m) clamped to [0, W].  When segment ids
+ * are given, entries of another segment are masked as well.  Masked entries
+ * are never selected and read -inf in the score output.
+ *
+ * The selection keeps, per row, the top_k valid entries ordered by score
+ * descending with ties going to the lower entry index, and pads with -1 when
+ * fewer than top_k entries are valid.
+ *
+ * Every loop runs in the order written: t from 0 to D-1 inside h from 0 to
+ * H-1, one rounding per operation (built with -ffp-contract=off, so no fused
+ * multiply-add).  The products of two bf16 values are exact in fp32; w times
+ * ReLU(logit) is rounded before it is added.  A float64 twin of the score
+ * (same loops in double) bounds the fp32 version's own rounding error.
+ *
+ * Pins: see tests/test_oracle.py (closed forms, a library special case,
+ * invariants, brute-force selection, the float64 twin).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static float bf16_value(uint16_t bits)
+{
+    /* A bfloat16 value is the upper half of the float32 with the same value. */
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static int64_t floor_div(int64_t a, int64_t b)
+{
+    int64_t q = a / b;
+    if ((a % b) != 0 && ((a < 0) != (b < 0)))
+        q -= 1;
+    return q;
+}
+
+/* Number of visible compressed entries for a row at absolute position pos. */
+static int64_t causal_threshold(int64_t pos, int64_t m, int64_t W)
+{
+    int64_t t = floor_div(pos + 1, m);
+    if (t < 0)
+        t = 0;
+    if (t > W)
+        t = W;
+    return t;
+}
+
+static int entry_is_valid(int64_t b, int64_t i, int64_t j, int64_t S, int64_t W, int64_t m,
+                          const int32_t *q_offset, const int32_t *q_seg, const int32_t *k_seg)
+{
+    int64_t pos = (q_offset ? (int64_t)q_offset[b] : 0) + i;
+    if (j >= causal_threshold(pos, m, W))
+        return 0;
+    if (q_seg && q_seg[b * S + i] != k_seg[b * W + j])
+        return 0;
+    return 1;
+}
+
+/*
+ * Scores of n_rows rows, fp32.  rows[r] = b*S + i names the row (rows == NULL
+ * means rows 0..n_rows-1).  out is [n_rows, W].  q is [B,H,S,D], k is
+ * [B,W,D], w is [B,S,H], all dense bf16 bit patterns.
+ */
+void csa_oracle_scores_f32(int64_t B, int64_t S, int64_t H, int64_t D, int64_t W, int64_t m,
+                           float scale, const uint16_t *q, const uint16_t *k, const uint16_t *w,
+                           const int32_t *q_offset, const int32_t *q_seg, const int32_t *k_seg,
+                           int64_t n_rows, const int64_t *rows, float *out)
+{
+    (void)B;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t row = rows ? rows[r] : r;
+        int64_t b = row / S, i = row % S;
+        for (int64_t j = 0; j < W; ++j) {
+            float *o = &out[r * W + j];
+            if (!entry_is_valid(b, i, j, S, W, m, q_offset, q_seg, k_seg)) {
+                *o = -INFINITY;
+                continue;
+            }
+            float s = 0.0f;
+            for (int64_t h = 0; h < H; ++h) {
+                float logit = 0.0f;
+                for (int64_t t = 0; t < D; ++t) {
+                    float qv = bf16_value(q[((b * H + h) * S + i) * D + t]);
+                    float kv = bf16_value(k[(b * W + j) * D + t]);
+                    logit = logit + qv * kv;
+                }
+                float relu = logit > 0.0f ? logit : 0.0f;
+                float wv = bf16_value(w[(b * S + i) * H + h]);
+                float term = wv * relu;
+                s = s + term;
+            }
+            s = scale * s;
+            *o = s + 0.0f; /* -0 becomes +0 */
+        }
+    }
+}
+
+/* The same scores computed in float64 throughout (inputs widened exactly). */
+void csa_oracle_scores_f64(int64_t B, int64_t S, int64_t H, int64_t D, int64_t W, int64_t m,
+                           double scale, const uint16_t *q, const uint16_t *k, const uint16_t *w,
+                           const int32_t *q_offset, const int32_t *q_seg, const int32_t *k_seg,
+                           int64_t n_rows, const int64_t *rows, double *out)
+{
+    (void)B;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t row = rows ? rows[r] : r;
+        int64_t b = row / S, i = row % S;
+        for (int64_t j = 0; j < W; ++j) {
+            double *o = &out[r * W + j];
+            if (!entry_is_valid(b, i, j, S, W, m, q_offset, q_seg, k_seg)) {
+                *o = -INFINITY;
+                continue;
+            }
+            double s = 0.0;
+            for (int64_t h = 0; h < H; ++h) {
+                double logit = 0.0;
+                for (int64_t t = 0; t < D; ++t) {
+                    double qv = (double)bf16_value(q[((b * H + h) * S + i) * D + t]);
+                    double kv = (double)bf16_value(k[(b * W + j) * D + t]);
+                    logit = logit + qv * kv;
+                }
+                double relu = logit > 0.0 ? logit : 0.0;
+                double wv = (double)bf16_value(w[(b * S + i) * H + h]);
+                s = s + wv * relu;
+            }
+            *o = scale * s + 0.0;
+        }
+    }
+}
+
+/* Validity mask only: 1 where (row, j) is a candidate, else 0.  [n_rows, W]. */
+void csa_oracle_valid(int64_t S, int64_t W, int64_t m, const int32_t *q_offset,
+                      const int32_t *q_seg, const int32_t *k_seg, int64_t n_rows,
+                      const int64_t *rows, uint8_t *out)
+{
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t row = rows ? rows[r] : r;
+        int64_t b = row / S, i = row % S;
+        for (int64_t j = 0; j < W; ++j)
+            out[r * W + j] = (uint8_t)entry_is_valid(b, i, j, S, W, m, q_offset, q_seg, k_seg);
+    }
+}
+
+typedef struct {
+    float score;
+    int32_t j;
+} candidate;
+
+/* Order: higher score first; equal scores -> lower entry index first. */
+static int candidate_order(const void *pa, const void *pb)
+{
+    const candidate *a = (const candidate *)pa, *b = (const candidate *)pb;
+    if (a->score > b->score)
+        return -1;
+    if (a->score < b->score)
+        return 1;
+    return (a->j > b->j) - (a->j < b->j);
+}
+
+/*
+ * Top-k of each row of a dense [rows, W] fp32 score matrix.  An entry whose
+ * score is -inf (masked) or NaN is never selected.  idx is [rows, top_k]:
+ * the selected entry indices in the candidate order above, then -1s.
+ */
+void csa_oracle_topk(int64_t rows, int64_t W, int64_t top_k, const float *scores, int32_t *idx)
+{
+#pragma omp parallel
+    {
+        candidate *buf = (candidate *)malloc(sizeof(candidate) * (size_t)(W > 0 ? W : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < rows; ++r) {
+            int64_t n = 0;
+            for (int64_t j = 0; j < W; ++j) {
+                float s = scores[r * W + j];
+                if (s == -INFINITY || s != s)
+                    continue;
+                buf[n].score = s;
+                buf[n].j = (int32_t)j;
+                ++n;
+            }
+            qsort(buf, (size_t)n, sizeof(candidate), candidate_order);
+            for (int64_t t = 0; t < top_k; ++t)
+                idx[r * top_k + t] = t < n ? buf[t].j : -1;
+        }
+        free(buf);
+    }
+}
+
+int csa_oracle_version(void) { return 1; }
