@@ -1,0 +1,146 @@
+/*
+ * csa_index.h -- C ABI of the MI355X (gfx950) CSA indexer score / top-k library.
+ *
+ * The operation (DeepSeek-V4 Compressed Sparse Attention indexer, the fused
+ * "StreamIndex" score of MaxText PR #5079 "Add StreamIndex Kernel for CSA",
+ * PR description and the BlockSpec review): for batch b, query row i and
+ * compressed key entry j,
+ *
+ *     score[b,i,j] = scale * sum_h w[b,i,h] * ReLU( sum_t q[b,h,i,t] * k[b,j,t] )
+ *
+ * with bf16 inputs and fp32 accumulation (the same PR's commit that chunks the
+ * head accumulation and runs bf16 einsums with float32 accumulation).
+ *
+ * Masks (MaxText PR #4915 "DSV4: Add indexer_save_selection and
+ * indexer_sharded_topk", inline review of the indexer's future and segment
+ * masks): with absolute row position p = q_offset[b] + i and compress rate m,
+ * entry j is a future entry when j >= clamp(floor((p+1)/m), 0, W).  When
+ * segment ids are given, entry j is also masked when k_seg[b,j] != q_seg[b,i].
+ * A masked entry reads -inf in a score output and is never selected.
+ *
+ * Selection (same PR, description: masking and top-k selection consumed by
+ * the sparse attention): per row, the top_k unmasked entries ordered by score
+ * descending, equal scores going to the lower j, then -1 padding when fewer
+ * than top_k entries are unmasked.  -0 and +0 scores compare equal.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates and frees nothing, never synchronises, and keeps no pointer
+ *    after returning.  Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    default stream); buffers must stay alive until it completes.
+ *  - Arguments are checked on the host before anything is enqueued.  On any
+ *    error nothing is enqueued, the function returns a non-zero status and
+ *    csa_last_error() describes the problem.  Shapes the kernels do not
+ *    implement return CSA_ERR_UNSUPPORTED; there is no silent fallback.
+ *  - bf16 tensors are passed as 16-bit bfloat16 patterns.
+ *  - Device-resident q_offset / q_seg / k_seg values are never trusted for
+ *    addressing: any int32 value is memory-safe (thresholds are clamped).
+ *  - Functions never throw and are safe to call from several host threads.
+ */
+#ifndef CSA_INDEX_H
+#define CSA_INDEX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum csa_status {
+    CSA_OK = 0,
+    CSA_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size, inconsistent masks */
+    CSA_ERR_UNSUPPORTED = 2, /* a shape or stride the kernels do not implement        */
+    CSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required             */
+    CSA_ERR_DEVICE = 4       /* the HIP runtime reported an error when launching       */
+} csa_status;
+
+/* Execution plan.  AUTO picks by shape; the others force one plan (every plan
+ * computes bit-identical scores and selections). */
+typedef enum csa_plan {
+    CSA_PLAN_AUTO = 0,
+    CSA_PLAN_ROW_TILES = 1, /* workgroups own blocks of query rows and walk K tiles    */
+    CSA_PLAN_SPLIT_ROWS = 2 /* long rows split over workgroups (decode), then a top-k pass */
+} csa_plan;
+
+/*
+ * Problem description.  Element strides (not bytes).  The innermost dimension
+ * is contiguous: D for q and k, H for w.
+ *   q : [B,H,S,D] bf16 at q + b*q_sb + h*q_sh + i*q_ss + t
+ *       (head-major q has q_sh = S*D, q_ss = D; sequence-major [B,S,H,D] has
+ *        q_sh = D, q_ss = H*D)
+ *   k : [B,W,D] bf16 at k + b*k_sb + j*k_sw + t   (decode: W = cache capacity)
+ *   w : [B,S,H] bf16 at w + b*w_sb + i*w_ss + h
+ * Supported: D in {32, 64, 128}; 1 <= H <= 128; q and k 16-byte aligned with
+ * strides that are multiples of 8 elements; W <= 2^30; m >= 1; finite scale.
+ */
+typedef struct csa_index_problem {
+    int32_t B, S, H, D, W;
+    int32_t compress_rate; /* m */
+    float scale;
+    int32_t plan;          /* csa_plan */
+    int64_t q_sb, q_sh, q_ss;
+    int64_t k_sb, k_sw;
+    int64_t w_sb, w_ss;
+} csa_index_problem;
+
+/* Optional masks (device pointers).  masks == NULL means all fields NULL. */
+typedef struct csa_index_masks {
+    const int32_t *q_offset; /* [B] absolute position of row 0; NULL => 0          */
+    const int32_t *q_seg;    /* [B,S] dense segment id of each row; NULL => none    */
+    const int32_t *k_seg;    /* [B,W] dense segment id of each entry; NULL iff q_seg */
+} csa_index_masks;
+
+/*
+ * Masked scores.  scores: [B,S,W] fp32, dense, 4-byte aligned; every element
+ * is written (masked = -inf).
+ */
+csa_status csa_index_score(const csa_index_problem *p, const void *q, const void *k, const void *w,
+                           const csa_index_masks *masks, float *scores, void *stream);
+
+/*
+ * Top-k of each row of a dense fp32 matrix scores [rows, W] (row stride W).
+ * Entries equal to -inf or NaN are never selected.  idx: [rows, top_k] int32.
+ * 1 <= top_k <= 2048.  Needs no workspace today: pass NULL / 0 (a size query
+ * is provided so callers need not change if that ever changes).
+ */
+csa_status csa_index_topk(int64_t rows, int32_t W, int32_t top_k, const float *scores,
+                          int32_t *idx, void *workspace, size_t workspace_bytes, void *stream);
+
+csa_status csa_index_topk_workspace_size(int64_t rows, int32_t W, int32_t top_k, size_t *bytes);
+
+/*
+ * Fused score + selection.  idx: [B,S,top_k] int32 (dense).  scores: optional
+ * [B,S,W] fp32 output (NULL = not written; the score matrix then never reaches
+ * HBM on the row-tile plan).  workspace: device memory of at least
+ * csa_index_workspace_size() bytes (may be NULL when that size is 0), 256-byte
+ * aligned.  1 <= top_k <= 2048.
+ */
+csa_status csa_index_select(const csa_index_problem *p, const void *q, const void *k, const void *w,
+                            const csa_index_masks *masks, int32_t top_k, int32_t *idx, float *scores,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes csa_index_select needs for this problem when scores == NULL
+ * (0 when it needs none).  Host-only; checks the arguments like the call. */
+csa_status csa_index_workspace_size(const csa_index_problem *p, int32_t top_k, size_t *bytes);
+
+/* Plan the library would run for this problem (CSA_PLAN_ROW_TILES or
+ * CSA_PLAN_SPLIT_ROWS), or -1 if the problem is invalid.  Host-only. */
+int32_t csa_index_resolve_plan(const csa_index_problem *p);
+
+/* Static description of a status code. */
+const char *csa_status_string(csa_status s);
+
+/* Detail of the last error on the calling host thread ("" if none). */
+const char *csa_last_error(void);
+
+/* ABI version of this header (bumped on incompatible change). */
+int32_t csa_index_abi_version(void);
+
+#define CSA_INDEX_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_INDEX_H */

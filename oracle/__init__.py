@@ -58,6 +58,7 @@ def _load():
     lib.csa_oracle_topk.argtypes = [i64, i64, i64, vp, vp]
     lib.csa_oracle_topk.restype = None
     lib.csa_oracle_version.restype = ctypes.c_int
+    lib.csa_oracle_threads.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -131,6 +132,11 @@ def topk(score_rows: np.ndarray, top_k: int) -> np.ndarray:
     out = np.empty((s.shape[0], top_k), dtype=np.int32)
     _load().csa_oracle_topk(s.shape[0], s.shape[1], top_k, _ptr(s), _ptr(out))
     return out
+
+
+def threads() -> int:
+    """Number of OpenMP threads the oracle runs on."""
+    return int(_load().csa_oracle_threads())
 
 
 def select(P, rows: Optional[Sequence[int]] = None):

@@ -35,6 +35,7 @@
  * invariants, brute-force selection, the float64 twin).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -211,3 +212,6 @@ void csa_oracle_topk(int64_t rows, int64_t W, int64_t top_k, const float *scores
 }
 
 int csa_oracle_version(void) { return 1; }
+
+/* OpenMP threads the oracle's parallel loops use. */
+int csa_oracle_threads(void) { return omp_get_max_threads(); }

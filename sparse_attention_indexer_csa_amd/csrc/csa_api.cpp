@@ -1,0 +1,352 @@
+// C ABI of the indexer library: argument checks (host only, before any HIP
+// call), plan choice, and kernel dispatch.  See include/csa_index.h.
+#include "csa_index.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "csa_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+csa_status fail(csa_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+csa_status ok()
+{
+    g_last_error.clear();
+    return CSA_OK;
+}
+
+constexpr int kMaxTopK = 2048;
+constexpr int kMaxW = 1 << 30;
+constexpr int kNumCUs = 256; // MI355X; only used to choose a plan
+// A row-tile launch with fewer workgroups than this leaves the chip idle.
+constexpr int64_t kMinRowBlocks = 2 * kNumCUs;
+// Rows shorter than this are not worth splitting.
+constexpr int kMinSplitW = 2048;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int head_blocks(int H)
+{
+    int hb = (H + 15) / 16;
+    int p = 1;
+    while (p < hb)
+        p <<= 1;
+    return p;
+}
+
+struct Checked {
+    int64_t rows = 0; // B*S
+    int HB = 0;
+    int plan = 0;
+};
+
+csa_status check_problem(const csa_index_problem *p, Checked &c)
+{
+    if (!p)
+        return fail(CSA_ERR_INVALID_ARG, "problem descriptor is NULL");
+    if (p->B < 0 || p->S < 0 || p->W < 0)
+        return fail(CSA_ERR_INVALID_ARG, "negative size (B=%d S=%d W=%d)", p->B, p->S, p->W);
+    if (p->H < 1 || p->D < 1)
+        return fail(CSA_ERR_INVALID_ARG, "H and D must be >= 1 (H=%d D=%d)", p->H, p->D);
+    if (p->compress_rate < 1)
+        return fail(CSA_ERR_INVALID_ARG, "compress_rate must be >= 1 (got %d)", p->compress_rate);
+    if (!std::isfinite(p->scale))
+        return fail(CSA_ERR_INVALID_ARG, "scale must be finite");
+    if (p->plan < CSA_PLAN_AUTO || p->plan > CSA_PLAN_SPLIT_ROWS)
+        return fail(CSA_ERR_INVALID_ARG, "unknown plan %d", p->plan);
+    if (p->D != 32 && p->D != 64 && p->D != 128)
+        return fail(CSA_ERR_UNSUPPORTED, "D=%d not implemented (D must be 32, 64 or 128)", p->D);
+    if (p->H > 128)
+        return fail(CSA_ERR_UNSUPPORTED, "H=%d not implemented (H <= 128)", p->H);
+    if (p->W > kMaxW)
+        return fail(CSA_ERR_UNSUPPORTED, "W=%d above the supported maximum %d", p->W, kMaxW);
+    if (p->q_sb < 0 || p->q_sh < 0 || p->q_ss < 0 || p->k_sb < 0 || p->k_sw < 0 || p->w_sb < 0 || p->w_ss < 0)
+        return fail(CSA_ERR_INVALID_ARG, "strides must be non-negative");
+    if ((p->q_sb | p->q_sh | p->q_ss | p->k_sb | p->k_sw) % 8 != 0)
+        return fail(CSA_ERR_UNSUPPORTED, "q and k strides must be multiples of 8 elements (16-byte rows)");
+    c.rows = (int64_t)p->B * p->S;
+    c.HB = head_blocks(p->H);
+    int64_t row_blocks = (int64_t)p->B * ((p->S + csa::kRowsPerBlock - 1) / csa::kRowsPerBlock);
+    int plan = p->plan;
+    if (plan == CSA_PLAN_AUTO)
+        plan = (row_blocks < kMinRowBlocks && p->W >= kMinSplitW) ? CSA_PLAN_SPLIT_ROWS : CSA_PLAN_ROW_TILES;
+    c.plan = plan;
+    // grid sizes must fit a 32-bit launch
+    int64_t chunks = (p->W + csa::kSplitChunk - 1) / csa::kSplitChunk;
+    if (row_blocks > 0x7FFFFFFF || c.rows * (chunks > 0 ? chunks : 1) > 0x7FFFFFFF)
+        return fail(CSA_ERR_UNSUPPORTED, "problem too large for one launch");
+    return CSA_OK;
+}
+
+csa_status check_inputs(const csa_index_problem *p, const Checked &c, const void *q, const void *k, const void *w,
+                        const csa_index_masks *masks)
+{
+    if (c.rows > 0) {
+        if (!q || !w)
+            return fail(CSA_ERR_INVALID_ARG, "q and w must be non-NULL");
+        if (!aligned(q, 16))
+            return fail(CSA_ERR_INVALID_ARG, "q must be 16-byte aligned");
+        if (!aligned(w, 2))
+            return fail(CSA_ERR_INVALID_ARG, "w must be 2-byte aligned");
+    }
+    if ((int64_t)p->B * p->W > 0) {
+        if (!k)
+            return fail(CSA_ERR_INVALID_ARG, "k must be non-NULL");
+        if (!aligned(k, 16))
+            return fail(CSA_ERR_INVALID_ARG, "k must be 16-byte aligned");
+    }
+    if (masks) {
+        if ((masks->q_seg == nullptr) != (masks->k_seg == nullptr))
+            return fail(CSA_ERR_INVALID_ARG, "q_seg and k_seg must be both NULL or both set");
+        if (!aligned(masks->q_offset, 4) || !aligned(masks->q_seg, 4) || !aligned(masks->k_seg, 4))
+            return fail(CSA_ERR_INVALID_ARG, "mask arrays must be 4-byte aligned");
+    }
+    return CSA_OK;
+}
+
+csa::KernelArgs make_args(const csa_index_problem *p, const Checked &c, const void *q, const void *k, const void *w,
+                          const csa_index_masks *masks)
+{
+    csa::KernelArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.w = static_cast<const uint16_t *>(w);
+    if (masks) {
+        a.q_offset = masks->q_offset;
+        a.q_seg = masks->q_seg;
+        a.k_seg = masks->k_seg;
+    }
+    a.q_sb = p->q_sb;
+    a.q_sh = p->q_sh;
+    a.q_ss = p->q_ss;
+    a.k_sb = p->k_sb;
+    a.k_sw = p->k_sw;
+    a.w_sb = p->w_sb;
+    a.w_ss = p->w_ss;
+    a.rows = c.rows;
+    a.B = p->B;
+    a.S = p->S;
+    a.H = p->H;
+    a.W = p->W;
+    a.m = p->compress_rate;
+    a.scale = p->scale;
+    a.n_row_blocks = (p->S + csa::kRowsPerBlock - 1) / csa::kRowsPerBlock;
+    a.n_chunks = (p->W + csa::kSplitChunk - 1) / csa::kSplitChunk;
+    return a;
+}
+
+csa_status device_lds_limit(size_t need, const char *what)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(CSA_ERR_DEVICE, "hipGetDevice failed");
+    int lim = 0;
+    if (hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return fail(CSA_ERR_DEVICE, "cannot query the LDS limit");
+    if (need > (size_t)lim)
+        return fail(CSA_ERR_UNSUPPORTED, "%s needs %zu bytes of LDS per workgroup, device allows %d", what, need, lim);
+    return CSA_OK;
+}
+
+csa_status launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(CSA_ERR_DEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+size_t select_workspace(const csa_index_problem *p, const Checked &c)
+{
+    if (c.plan != CSA_PLAN_SPLIT_ROWS)
+        return 0;
+    return (size_t)c.rows * (size_t)p->W * sizeof(float);
+}
+
+} // namespace
+
+extern "C" {
+
+int32_t csa_index_abi_version(void) { return CSA_INDEX_ABI_VERSION; }
+
+const char *csa_status_string(csa_status s)
+{
+    switch (s) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_INVALID_ARG: return "invalid argument";
+    case CSA_ERR_UNSUPPORTED: return "unsupported shape or layout";
+    case CSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA_ERR_DEVICE: return "device or launch error";
+    default: return "unknown status";
+    }
+}
+
+const char *csa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t csa_index_resolve_plan(const csa_index_problem *p)
+{
+    Checked c;
+    if (check_problem(p, c) != CSA_OK)
+        return -1;
+    return c.plan;
+}
+
+csa_status csa_index_workspace_size(const csa_index_problem *p, int32_t top_k, size_t *bytes)
+{
+    if (!bytes)
+        return fail(CSA_ERR_INVALID_ARG, "bytes is NULL");
+    Checked c;
+    csa_status st = check_problem(p, c);
+    if (st != CSA_OK)
+        return st;
+    if (top_k < 1 || top_k > kMaxTopK)
+        return fail(CSA_ERR_UNSUPPORTED, "top_k=%d outside [1, %d]", top_k, kMaxTopK);
+    *bytes = select_workspace(p, c);
+    return ok();
+}
+
+csa_status csa_index_topk_workspace_size(int64_t rows, int32_t W, int32_t top_k, size_t *bytes)
+{
+    if (!bytes)
+        return fail(CSA_ERR_INVALID_ARG, "bytes is NULL");
+    if (rows < 0 || W < 0)
+        return fail(CSA_ERR_INVALID_ARG, "negative size");
+    if (top_k < 1 || top_k > kMaxTopK)
+        return fail(CSA_ERR_UNSUPPORTED, "top_k=%d outside [1, %d]", top_k, kMaxTopK);
+    *bytes = 0;
+    return ok();
+}
+
+csa_status csa_index_score(const csa_index_problem *p, const void *q, const void *k, const void *w,
+                           const csa_index_masks *masks, float *scores, void *stream)
+{
+    Checked c;
+    csa_status st = check_problem(p, c);
+    if (st != CSA_OK)
+        return st;
+    if ((st = check_inputs(p, c, q, k, w, masks)) != CSA_OK)
+        return st;
+    if (c.rows * p->W == 0)
+        return ok();
+    if (!scores || !aligned(scores, 4))
+        return fail(CSA_ERR_INVALID_ARG, "scores must be a non-NULL, 4-byte aligned pointer");
+    csa::KernelArgs a = make_args(p, c, q, k, w, masks);
+    a.scores = scores;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (c.plan == CSA_PLAN_SPLIT_ROWS) {
+        a.full_rows = 1;
+        return launched(csa::launch_split(p->D, c.HB, a, s), "split score");
+    }
+    size_t lds = csa::rows_lds_bytes(p->D, csa::kModeScores, 0);
+    return launched(csa::launch_rows(p->D, c.HB, csa::kModeScores, a, lds, s), "row-tile score");
+}
+
+csa_status csa_index_topk(int64_t rows, int32_t W, int32_t top_k, const float *scores, int32_t *idx,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    if (rows < 0 || W < 0)
+        return fail(CSA_ERR_INVALID_ARG, "negative size (rows=%lld W=%d)", (long long)rows, W);
+    if (top_k < 1 || top_k > kMaxTopK)
+        return fail(CSA_ERR_UNSUPPORTED, "top_k=%d outside [1, %d]", top_k, kMaxTopK);
+    if (W > kMaxW)
+        return fail(CSA_ERR_UNSUPPORTED, "W=%d above the supported maximum %d", W, kMaxW);
+    if (rows == 0)
+        return ok();
+    if (rows > (int64_t)0x7FFFFFFF * csa::kTopkWaves)
+        return fail(CSA_ERR_UNSUPPORTED, "too many rows for one launch");
+    if (!idx || !aligned(idx, 4))
+        return fail(CSA_ERR_INVALID_ARG, "idx must be a non-NULL, 4-byte aligned pointer");
+    if (W > 0 && (!scores || !aligned(scores, 4)))
+        return fail(CSA_ERR_INVALID_ARG, "scores must be a non-NULL, 4-byte aligned pointer");
+    csa::KernelArgs a{};
+    a.scores = const_cast<float *>(scores);
+    a.idx = idx;
+    a.rows = rows;
+    a.W = W;
+    a.S = 1;
+    a.m = 1;
+    a.top_k = top_k;
+    a.cap = csa::topk_capacity(top_k);
+    size_t lds = csa::topk_lds_bytes(a.cap);
+    csa_status st = device_lds_limit(lds, "top-k");
+    if (st != CSA_OK)
+        return st;
+    return launched(csa::launch_topk(a, lds, static_cast<hipStream_t>(stream)), "top-k");
+}
+
+csa_status csa_index_select(const csa_index_problem *p, const void *q, const void *k, const void *w,
+                            const csa_index_masks *masks, int32_t top_k, int32_t *idx, float *scores,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    Checked c;
+    csa_status st = check_problem(p, c);
+    if (st != CSA_OK)
+        return st;
+    if ((st = check_inputs(p, c, q, k, w, masks)) != CSA_OK)
+        return st;
+    if (top_k < 1 || top_k > kMaxTopK)
+        return fail(CSA_ERR_UNSUPPORTED, "top_k=%d outside [1, %d]", top_k, kMaxTopK);
+    if (c.rows == 0)
+        return ok();
+    if (!idx || !aligned(idx, 4))
+        return fail(CSA_ERR_INVALID_ARG, "idx must be a non-NULL, 4-byte aligned pointer");
+    if (scores && !aligned(scores, 4))
+        return fail(CSA_ERR_INVALID_ARG, "scores must be 4-byte aligned");
+    csa::KernelArgs a = make_args(p, c, q, k, w, masks);
+    a.idx = idx;
+    a.top_k = top_k;
+    a.cap = csa::topk_capacity(top_k);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (c.plan == CSA_PLAN_SPLIT_ROWS) {
+        float *buf = scores;
+        if (!buf) {
+            size_t need = select_workspace(p, c);
+            if (need > 0 && (!workspace || workspace_bytes < need))
+                return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                            workspace ? workspace_bytes : (size_t)0);
+            if (!aligned(workspace, 256))
+                return fail(CSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+            buf = static_cast<float *>(workspace);
+        }
+        size_t lds = csa::topk_lds_bytes(a.cap);
+        if ((st = device_lds_limit(lds, "top-k")) != CSA_OK)
+            return st;
+        a.scores = buf;
+        a.full_rows = scores ? 1 : 0;
+        if (p->W > 0) {
+            hipError_t e = csa::launch_split(p->D, c.HB, a, s);
+            if (e != hipSuccess)
+                return launched(e, "split score");
+        }
+        a.limit_rows = 1;
+        return launched(csa::launch_topk(a, lds, s), "top-k");
+    }
+
+    const int mode = csa::kModeSelect | (scores ? csa::kModeScores : 0);
+    size_t lds = csa::rows_lds_bytes(p->D, mode, a.cap);
+    if ((st = device_lds_limit(lds, "row-tile select")) != CSA_OK)
+        return st;
+    a.scores = scores;
+    return launched(csa::launch_rows(p->D, c.HB, mode, a, lds, s), "row-tile select");
+}
+
+} // extern "C"

@@ -1,0 +1,58 @@
+// Launch interface between the C ABI (csa_api.cpp) and the kernels
+// (csa_kernels.hip).  Host-side only declarations plus the argument block
+// the kernels receive by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct KernelArgs {
+    const uint16_t *q;
+    const uint16_t *k;
+    const uint16_t *w;
+    const int32_t *q_offset;
+    const int32_t *q_seg;
+    const int32_t *k_seg;
+    float *scores;   // [rows, W] (rows = B*S), dense
+    int32_t *idx;    // [rows, top_k]
+    int64_t q_sb, q_sh, q_ss;
+    int64_t k_sb, k_sw;
+    int64_t w_sb, w_ss;
+    int64_t rows;    // B*S (top-k kernel: number of rows)
+    int32_t B, S, H, W, m;
+    int32_t top_k, cap;
+    int32_t n_row_blocks; // row-tile plan: ceil(S / rows per workgroup)
+    int32_t n_chunks;     // split plan: workgroups per row
+    int32_t full_rows;    // split plan: write every score of the row (-inf past the visible prefix)
+    int32_t limit_rows;   // top-k kernel: rows end at their visible prefix (q_offset, m)
+    float scale;
+};
+
+// Row-tile plan geometry.
+constexpr int kRowWaves = 4;            // waves per workgroup, one query row each
+constexpr int kRowsPerBlock = kRowWaves;
+constexpr int kTileEntries = 64;        // compressed entries per LDS K tile
+// Split plan geometry.
+constexpr int kSplitWaves = 4;
+constexpr int kSplitSubtiles = 16;      // 16-entry subtiles per wave
+constexpr int kSplitChunk = kSplitWaves * kSplitSubtiles * 16;
+// Top-k kernel geometry.
+constexpr int kTopkWaves = 4;
+
+enum { kModeScores = 1, kModeSelect = 2 };
+
+// Candidate-buffer capacity of the streaming top-k for a given k (room for at
+// least one more 64-pair push after a compaction down to k).
+__host__ __device__ constexpr int topk_capacity(int k) { return ((k + 63) / 64) * 64 + 512; }
+
+size_t rows_lds_bytes(int D, int mode, int cap);
+size_t topk_lds_bytes(int cap);
+
+// Each returns hipSuccess or the launch error; nothing is synchronised.
+hipError_t launch_rows(int D, int HB, int mode, const KernelArgs &a, size_t lds, hipStream_t s);
+hipError_t launch_split(int D, int HB, const KernelArgs &a, hipStream_t s);
+hipError_t launch_topk(const KernelArgs &a, size_t lds, hipStream_t s);
+
+} // namespace csa

@@ -8,6 +8,7 @@ library) and the benchmark take their inputs from here.
 """
 
 from .inputs import (  # noqa: F401
+    CONFIG_TITLES,
     CONFIGS,
     Problem,
     bf16_bits_to_f32,

@@ -1,0 +1,260 @@
+"""GPU parity: the HIP library against the CPU oracle, element by element.
+
+Runs through the binding (and so through the C ABI).  Integer-grid workloads
+must match bit for bit; Gaussian ones within the stated tolerance (see
+gpu_util).  Full-size workloads run in the launch configuration the benchmark
+times and are compared on sampled rows, which the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (assert_scores_close, assert_topk_match, dev_problem, gpu_score, gpu_select, to_np)
+from synth import bf16_bits_to_f32, f32_to_bf16_bits, make_config, make_problem
+
+import sparse_attention_indexer_csa_amd as csa
+
+pytestmark = pytest.mark.gpu
+
+PLANS = ["row_tiles", "split_rows"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    csa.load_library()
+    oracle.build(force=False)
+
+
+def _check_full(P, plan, exact, with_scores=True):
+    s_o, i_o = oracle.select(P)
+    idx, sc = gpu_select(P, plan=plan, return_scores=True)
+    sc2 = gpu_score(P, plan=plan)
+    idx_only = gpu_select(P, plan=plan)
+    assert_scores_close(to_np(sc).reshape(P.rows, P.W), s_o, exact=exact, what=f"{P.name} select scores")
+    assert_scores_close(to_np(sc2).reshape(P.rows, P.W), s_o, exact=exact, what=f"{P.name} score")
+    assert_topk_match(to_np(idx).reshape(P.rows, -1), i_o, s_o, exact=exact, what=f"{P.name} select")
+    # the fused selection without a score output is the same selection
+    np.testing.assert_array_equal(to_np(idx_only), to_np(idx))
+    return s_o, i_o
+
+
+# --- the named workloads -------------------------------------------------------------
+
+@pytest.mark.parametrize("plan", PLANS)
+def test_tiny_integer_grid_exact(plan):
+    _check_full(make_config("c1"), plan, exact=True)
+
+
+def test_mid_integer_grid_exact():
+    _check_full(make_config("c2int"), "auto", exact=True)
+
+
+def test_mid_gaussian_tolerance():
+    _check_full(make_config("c2"), "auto", exact=False)
+
+
+def _sample_rows(S, B=1, extra=()):
+    rows = set()
+    for b in range(B):
+        for i in list(range(0, 8)) + list(range(2040, 2060)) + list(np.linspace(0, S - 1, 24).astype(int)) + \
+                [S - 2, S - 1] + list(extra):
+            if 0 <= i < S:
+                rows.add(b * S + int(i))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def test_long_prefill_full_size_sampled():
+    """seq-16384 prefill in the benchmark's launch configuration: fused select
+    (no score output) and the scores-only call, checked on sampled rows."""
+    P = make_config("c3")
+    d = dev_problem(P)
+    idx = to_np(gpu_select(P, dev=d)).reshape(P.rows, -1)
+    sc = to_np(gpu_score(P, dev=d)).reshape(P.rows, P.W)
+    rows = _sample_rows(P.S)
+    s_o, i_o = oracle.select(P, rows)
+    assert_scores_close(sc[rows], s_o, what="c3 score")
+    assert_topk_match(idx[rows], i_o, s_o, what="c3 select")
+    # every row: count of selected = min(k, visible), no -1 before the end
+    nvis = np.minimum((np.arange(P.S) + 1) // P.m, P.W)
+    cnt = (idx >= 0).sum(axis=1)
+    np.testing.assert_array_equal(cnt, np.minimum(nvis, P.top_k))
+
+
+@pytest.mark.parametrize("name", ["c4", "c4aligned"])
+def test_packed_segments_full_size_sampled(name):
+    P = make_config(name)
+    d = dev_problem(P)
+    idx = to_np(gpu_select(P, dev=d)).reshape(P.rows, -1)
+    sc = to_np(gpu_score(P, dev=d)).reshape(P.rows, P.W)
+    rows = _sample_rows(P.S, P.B, extra=np.where(np.diff(P.q_seg[0]) != 0)[0].tolist())
+    s_o, i_o = oracle.select(P, rows)
+    assert_scores_close(sc[rows], s_o, what=f"{name} score")
+    assert_topk_match(idx[rows], i_o, s_o, what=f"{name} select")
+
+
+def test_decode_full():
+    """B=64 decode rows over a 32768-entry cache, all rows checked."""
+    P = make_config("c5")
+    d = dev_problem(P)
+    assert csa.resolve_plan(d["q"], d["k"], d["w"], P.m) == "split_rows"
+    s_o, i_o = oracle.select(P)
+    idx = to_np(gpu_select(P, dev=d)).reshape(P.rows, -1)
+    idx2, sc = gpu_select(P, dev=d, return_scores=True)
+    assert_scores_close(to_np(sc).reshape(P.rows, P.W), s_o, what="c5 scores")
+    assert_topk_match(idx, i_o, s_o, what="c5 select")
+    np.testing.assert_array_equal(to_np(idx2).reshape(P.rows, -1), idx)
+    # the row-tile plan computes the very same bits
+    idx_rt = to_np(gpu_select(P, plan="row_tiles", dev=d)).reshape(P.rows, -1)
+    np.testing.assert_array_equal(idx_rt, idx)
+
+
+# --- selection given scores, and fused == two-pass ----------------------------------------
+
+def test_topk_exact_on_oracle_scores():
+    """The top-k kernel is exact on any fp32 input: on the oracle's own scores
+    it reproduces the oracle's selection bit for bit (ties, -0, -inf, NaN)."""
+    P = make_config("c2")
+    s_o, i_o = oracle.select(P)
+    got = to_np(csa.topk(torch.from_numpy(s_o).cuda(), P.top_k))
+    np.testing.assert_array_equal(got, i_o)
+    rng = np.random.default_rng(3)
+    s = rng.choice(np.array([-2.0, -0.0, 0.0, 0.5, 0.5, 1.0, 3.0], np.float32), size=(300, 1500))
+    s[rng.random(s.shape) < 0.2] = -np.inf
+    s[rng.random(s.shape) < 0.01] = np.nan
+    s[5] = -np.inf
+    for k in (1, 7, 64, 512, 700, 2048):
+        np.testing.assert_array_equal(to_np(csa.topk(torch.from_numpy(s).cuda(), k)), oracle.topk(s, k), err_msg=f"k={k}")
+
+
+@pytest.mark.parametrize("name,plan", [("c2", "auto"), ("c4", "auto"), ("c5", "auto"), ("c5", "row_tiles")])
+def test_fused_select_equals_topk_of_scores(name, plan):
+    P = make_config(name)
+    d = dev_problem(P)
+    sc = gpu_score(P, plan=plan, dev=d)
+    two_pass = to_np(csa.topk(sc, P.top_k))
+    fused = to_np(gpu_select(P, plan=plan, dev=d))
+    np.testing.assert_array_equal(fused, two_pass)
+
+
+# --- invariants on the GPU -------------------------------------------------------------------
+
+@pytest.mark.parametrize("dist", ["int", "gauss"])
+def test_decode_row_equals_last_prefill_row(dist):
+    S, H, D, W, m, k = 1024, 64, 128, 256, 4, 64
+    P = make_problem(3, S, H, D, W, m, k, dist=dist, seed=31)
+    idx, sc = gpu_select(P, return_scores=True)
+    Q = make_problem(3, 1, H, D, W, m, k, dist=dist, seed=31)
+    Q.q = np.ascontiguousarray(P.q[:, :, S - 1:S])
+    Q.w = np.ascontiguousarray(P.w[:, S - 1:S])
+    Q.k = P.k.copy()
+    Q.q_offset = np.full(3, S - 1, np.int32)
+    for plan in PLANS:
+        idx1, sc1 = gpu_select(Q, plan=plan, return_scores=True)
+        np.testing.assert_array_equal(to_np(sc1)[:, 0], to_np(sc)[:, S - 1])
+        np.testing.assert_array_equal(to_np(idx1)[:, 0], to_np(idx)[:, S - 1])
+
+
+def test_future_keys_are_never_read():
+    """Keys past a row's visible prefix are poisoned; the outputs of rows that
+    cannot see them do not change (bitwise)."""
+    P = make_config("c2")
+    d = dev_problem(P)
+    idx, sc = gpu_select(P, dev=d, return_scores=True)
+    J0 = 600
+    kk = bf16_bits_to_f32(P.k).copy()
+    kk[0, J0:] = 30.0
+    d2 = dict(d)
+    d2["k"] = torch.from_numpy(f32_to_bf16_bits(kk).view(np.int16)).view(torch.bfloat16).cuda()
+    idx2, sc2 = gpu_select(P, dev=d2, return_scores=True)
+    rows = np.where(np.minimum((np.arange(P.S) + 1) // P.m, P.W) <= J0)[0]
+    np.testing.assert_array_equal(to_np(sc2)[0, rows], to_np(sc)[0, rows])
+    np.testing.assert_array_equal(to_np(idx2)[0, rows], to_np(idx)[0, rows])
+
+
+def test_deterministic():
+    P = make_config("c2")
+    d = dev_problem(P)
+    a1, s1 = gpu_select(P, dev=d, return_scores=True)
+    a2, s2 = gpu_select(P, dev=d, return_scores=True)
+    np.testing.assert_array_equal(to_np(a1), to_np(a2))
+    assert np.array_equal(to_np(s1).view(np.uint32), to_np(s2).view(np.uint32))
+
+
+def test_power_of_two_scale_is_exact():
+    P = make_problem(1, 512, 64, 128, 128, 4, 32, dist="gauss", seed=41)
+    _, s1 = gpu_select(P, return_scores=True)
+    P.scale = 0.25
+    i2, s2 = gpu_select(P, return_scores=True)
+    a, b = to_np(s1), to_np(s2)
+    fin = np.isfinite(a)
+    np.testing.assert_array_equal(b[fin], a[fin] * np.float32(0.25))
+    s_o, i_o = oracle.select(P)
+    assert_topk_match(to_np(i2).reshape(P.rows, -1), i_o, s_o, what="scaled")
+
+
+# --- layouts and edge shapes (integer grid: bitwise) --------------------------------------
+
+EDGE = [
+    # (B, S, H, D, W, m, top_k, q_offset)
+    (1, 13, 4, 32, 8, 4, 3, None),          # ragged rows, short
+    (2, 77, 1, 32, 19, 4, 5, None),         # one head
+    (1, 200, 20, 64, 50, 4, 16, None),      # heads not a multiple of 16
+    (1, 130, 100, 128, 40, 3, 7, None),     # 100 heads, compress rate 3
+    (1, 96, 128, 128, 24, 4, 8, None),      # 128 heads
+    (2, 150, 8, 128, 150, 1, 33, None),     # compress rate 1 (W = S)
+    (1, 64, 16, 32, 16, 4, 1, None),        # top_k = 1
+    (1, 64, 16, 32, 16, 4, 40, None),       # top_k > W
+    (2, 40, 16, 64, 300, 4, 20, [-9, 2000]),  # offsets: before the start / past the cache
+    (1, 9, 16, 128, 4096, 2, 2048, [6000]),  # top_k = 2048, buffer compactions
+    (3, 5, 16, 32, 0, 4, 4, None),          # empty cache
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[str(c[:7]) for c in EDGE])
+@pytest.mark.parametrize("plan", PLANS)
+def test_edge_shapes_exact(case, plan):
+    B, S, H, D, W, m, k, off = case
+    P = make_problem(B, S, H, D, W, m, k, dist="int", seed=sum(case[:7]),
+                     q_offset=None if off is None else np.array(off, np.int32))
+    s_o, i_o = oracle.select(P)
+    idx, sc = gpu_select(P, plan=plan, return_scores=True)
+    assert_topk_match(to_np(idx).reshape(P.rows, -1), i_o, s_o, exact=True, what=str(case))
+    if W > 0:
+        assert_scores_close(to_np(sc).reshape(P.rows, W), s_o, exact=True, what=str(case))
+        assert_scores_close(to_np(gpu_score(P, plan=plan)).reshape(P.rows, W), s_o, exact=True, what=str(case))
+
+
+def test_empty_batch_and_rows():
+    for B, S in ((0, 10), (2, 0)):
+        P = make_problem(B, S, 4, 32, 8, 4, 3, dist="int", seed=1)
+        idx = gpu_select(P)
+        assert tuple(idx.shape) == (B, S, 3)
+
+
+def test_segments_exact_integer_grid():
+    P = make_problem(3, 300, 16, 64, 75, 4, 12, dist="int", seed=5, segments="random")
+    for plan in PLANS:
+        s_o, i_o = oracle.select(P)
+        idx, sc = gpu_select(P, plan=plan, return_scores=True)
+        assert_scores_close(to_np(sc).reshape(P.rows, P.W), s_o, exact=True, what=f"segments {plan}")
+        assert_topk_match(to_np(idx).reshape(P.rows, -1), i_o, s_o, exact=True, what=f"segments {plan}")
+
+
+def test_sequence_major_q_and_padded_k_rows():
+    """q given as a permuted [B,S,H,D] tensor and k with a row pitch wider
+    than D give the same bits as dense head-major inputs."""
+    P = make_problem(2, 96, 16, 64, 24, 4, 6, dist="gauss", seed=8)
+    d = dev_problem(P)
+    ref_i, ref_s = gpu_select(P, dev=d, return_scores=True)
+    d2 = dev_problem(P, layout="seq_major")
+    assert d2["q"].stride(1) == P.D and d2["q"].stride(2) == P.H * P.D
+    kb = torch.zeros(P.B, P.W, P.D + 8, dtype=torch.bfloat16, device="cuda")
+    kb[:, :, :P.D] = d["k"]
+    d2["k"] = kb[:, :, :P.D]
+    i2, s2 = gpu_select(P, dev=d2, return_scores=True)
+    np.testing.assert_array_equal(to_np(i2), to_np(ref_i))
+    assert np.array_equal(to_np(s2).view(np.uint32), to_np(ref_s).view(np.uint32))
