@@ -36,6 +36,8 @@ def command(out: str = LIB, extra: list | None = None) -> list:
     return [
         hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in VGPRs: no AGPR <-> VGPR copies before the epilogue
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-function",
         f"-I{INCLUDE}", f"-I{CSRC}",
         *[os.path.join(CSRC, s) for s in SOURCES],

@@ -42,9 +42,10 @@ constexpr int kMinSplitW = 2048;
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// 32-head MFMA blocks, rounded up to a power of two (1, 2 or 4).
 int head_blocks(int H)
 {
-    int hb = (H + 15) / 16;
+    int hb = (H + 31) / 32;
     int p = 1;
     while (p < hb)
         p <<= 1;
@@ -172,6 +173,32 @@ csa_status launched(hipError_t e, const char *what)
     return ok();
 }
 
+int device_lds(int *lim)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return -1;
+    if (hipDeviceGetAttribute(lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return -1;
+    return 0;
+}
+
+// Top-k over rows of length up to W: the workgroup-per-row kernel for long
+// rows when its LDS fits, else one wave per row.
+csa_status launch_topk_rows(csa::KernelArgs &a, hipStream_t s)
+{
+    int lim = 0;
+    if (device_lds(&lim) != 0)
+        return fail(CSA_ERR_DEVICE, "cannot query the device's LDS limit");
+    size_t block_lds = csa::topk_block_lds_bytes(a.cap, a.top_k);
+    if (a.W >= csa::kTopkBlockMinLen && block_lds <= (size_t)lim)
+        return launched(csa::launch_topk_block(a, block_lds, s), "top-k");
+    size_t lds = csa::topk_lds_bytes(a.cap);
+    if (lds > (size_t)lim)
+        return fail(CSA_ERR_UNSUPPORTED, "top-k needs %zu bytes of LDS per workgroup, device allows %d", lds, lim);
+    return launched(csa::launch_topk(a, lds, s), "top-k");
+}
+
 size_t select_workspace(const csa_index_problem *p, const Checked &c)
 {
     if (c.plan != CSA_PLAN_SPLIT_ROWS)
@@ -285,11 +312,7 @@ csa_status csa_index_topk(int64_t rows, int32_t W, int32_t top_k, const float *s
     a.m = 1;
     a.top_k = top_k;
     a.cap = csa::topk_capacity(top_k);
-    size_t lds = csa::topk_lds_bytes(a.cap);
-    csa_status st = device_lds_limit(lds, "top-k");
-    if (st != CSA_OK)
-        return st;
-    return launched(csa::launch_topk(a, lds, static_cast<hipStream_t>(stream)), "top-k");
+    return launch_topk_rows(a, static_cast<hipStream_t>(stream));
 }
 
 csa_status csa_index_select(const csa_index_problem *p, const void *q, const void *k, const void *w,
@@ -327,9 +350,6 @@ csa_status csa_index_select(const csa_index_problem *p, const void *q, const voi
                 return fail(CSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
             buf = static_cast<float *>(workspace);
         }
-        size_t lds = csa::topk_lds_bytes(a.cap);
-        if ((st = device_lds_limit(lds, "top-k")) != CSA_OK)
-            return st;
         a.scores = buf;
         a.full_rows = scores ? 1 : 0;
         if (p->W > 0) {
@@ -338,7 +358,7 @@ csa_status csa_index_select(const csa_index_problem *p, const void *q, const voi
                 return launched(e, "split score");
         }
         a.limit_rows = 1;
-        return launched(csa::launch_topk(a, lds, s), "top-k");
+        return launch_topk_rows(a, s);
     }
 
     const int mode = csa::kModeSelect | (scores ? csa::kModeScores : 0);

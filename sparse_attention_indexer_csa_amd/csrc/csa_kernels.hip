@@ -1,5 +1,5 @@
 // gfx950 kernels of the CSA indexer: the row-tile score / fused select
-// kernel, the split-row score kernel for long rows, and the row top-k kernel.
+// kernel, the split-row score kernel for long rows, and the row top-k kernels.
 #include <math.h>
 
 #include "csa_device.hpp"
@@ -11,19 +11,44 @@ namespace csa {
 
 template <int D>
 struct TileGeom {
-    static constexpr int kKs = D / 32;                      // MFMA k-steps per entry
+    static constexpr int kKs = D / 16;                      // MFMA k-steps per entry
     static constexpr int kPitch = D + 8;                    // LDS row pitch (elements): +16 B
     static constexpr int kChunks = kTileEntries * D / 8;    // 16-byte pieces per tile
     static constexpr int kPerThread = kChunks / (kRowWaves * kWave);
-    static constexpr size_t kTileBytes = (size_t)kTileEntries * kPitch * 2;
+    static constexpr int kTileElems = kTileEntries * kPitch;
+    static constexpr size_t kTileBytes = (size_t)kTileElems * 2;
 };
+
+// Scores of the 64 entries j0 .. j0+63 of one row: lane l returns the
+// scaled score of entry j0 + l.  Subtiles (32 entries) flagged off are not
+// computed (their lanes return garbage that the caller masks).  `load(b, sub)`
+// fills the B fragments of subtile sub.
+template <int HB, int KS, typename LoadB>
+__device__ __forceinline__ float tile_scores(const RowOperand<HB, KS> &row, bool do0, bool do1, float scale,
+                                             LoadB load)
+{
+    float p0 = 0.0f, p1 = 0.0f;
+    if (do0) {
+        bf16x8 b[KS];
+        load(b, 0);
+        p0 = subtile_partial<HB, KS>(row, b);
+    }
+    if (do1) {
+        bf16x8 b[KS];
+        load(b, 1);
+        p1 = subtile_partial<HB, KS>(row, b);
+    }
+    return scaled_score(combine_halves(p0, p1), scale);
+}
 
 // ---------------------------------------------------------------------------
 // Row-tile plan.  A workgroup owns kRowsPerBlock consecutive query rows of one
 // batch row (one row per wave) and walks the compressed keys in tiles of
-// kTileEntries entries staged in LDS and shared by its waves.  Tiles past the
-// last row's visible prefix are never loaded.  Workgroups are issued from the
-// longest rows (largest i) down so that the causal tail finishes early.
+// kTileEntries entries, double-buffered in LDS and shared by its waves (one
+// barrier per tile; the next tile's global loads are in flight during the
+// current tile's MFMAs).  Tiles past the last row's visible prefix are never
+// loaded.  Workgroups are issued from the longest rows (largest i) down so
+// the causal tail finishes early.
 //
 // mode & kModeScores: every score of the rows is written (masked = -inf).
 // mode & kModeSelect: each wave streams its row's scores through a TopKRow
@@ -34,6 +59,8 @@ __global__ __launch_bounds__(kRowWaves * kWave) void rows_kernel(const KernelArg
 {
     using G = TileGeom<D>;
     constexpr int KS = G::kKs;
+    // up to 64 heads the pipelined loop fits the register file
+    constexpr bool PIPE = HB <= 2;
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t *ktile = reinterpret_cast<uint16_t *>(smem);
 
@@ -56,14 +83,32 @@ __global__ __launch_bounds__(kRowWaves * kWave) void rows_kernel(const KernelArg
     const int32_t *kseg = a.k_seg ? a.k_seg + (int64_t)b * a.W : nullptr;
     const int64_t row_id = (int64_t)b * a.S + i;
 
-    RowOperand<HB, KS> row;
-    if (active)
-        load_row<HB, KS>(row, a.q + b * a.q_sb + (int64_t)i * a.q_ss, a.q_sh, a.w + b * a.w_sb + (int64_t)i * a.w_ss,
-                         a.H);
+    // With segments, tiles before the first one that holds an entry of any
+    // row's segment are masked for the whole workgroup and are skipped.
+    int t_lo = 0;
+    if (kseg) {
+        __shared__ int first_tile[kRowWaves];
+        int ft = ntiles;
+        if (active) {
+            for (int t = 0; t < ntiles; ++t) {
+                const int j = t * kTileEntries + l;
+                if (ballot(j < thr && kseg[min(j, a.W - 1)] == qseg) != 0ull) {
+                    ft = t;
+                    break;
+                }
+            }
+        }
+        if (l == 0)
+            first_tile[wv] = ft;
+        __syncthreads();
+#pragma unroll
+        for (int w2 = 0; w2 < kRowWaves; ++w2)
+            t_lo = w2 == 0 ? first_tile[0] : min(t_lo, first_tile[w2]);
+    }
 
     TopKRow tk;
     if (MODE & kModeSelect) {
-        unsigned char *base = smem + G::kTileBytes + (size_t)wv * (1024 + (size_t)a.cap * 8);
+        unsigned char *base = smem + 2 * G::kTileBytes + (size_t)wv * (1024 + (size_t)a.cap * 8);
         uint32_t *hist = reinterpret_cast<uint32_t *>(base);
         uint32_t *key = hist + 256;
         topk_init(tk, key, key + a.cap, hist, a.cap, a.top_k);
@@ -76,67 +121,119 @@ __global__ __launch_bounds__(kRowWaves * kWave) void rows_kernel(const KernelArg
         for (int x = 0; x < G::kPerThread; ++x) {
             const int c = tid + x * kRowWaves * kWave;
             const int e = c / (D / 8), p = c % (D / 8);
-            const int j = t * kTileEntries + e;
-            pre[x] = (j < a.W) ? *reinterpret_cast<const u32x4 *>(kb + (int64_t)j * a.k_sw + p * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
+            // Entries past W are always masked: read a clamped in-bounds row
+            // instead of zero-filling, so no wait is needed before compute.
+            const int j = min(t * kTileEntries + e, a.W - 1);
+            pre[x] = *reinterpret_cast<const u32x4 *>(kb + (int64_t)j * a.k_sw + p * 8);
         }
     };
-    if (ntiles > 0)
-        fetch(0);
-
-    for (int t = 0; t < ntiles; ++t) {
-        __syncthreads();
+    auto stash = [&](int buf) {
+        uint16_t *dst = ktile + buf * G::kTileElems;
 #pragma unroll
         for (int x = 0; x < G::kPerThread; ++x) {
             const int c = tid + x * kRowWaves * kWave;
             const int e = c / (D / 8), p = c % (D / 8);
-            *reinterpret_cast<u32x4 *>(ktile + e * G::kPitch + p * 8) = pre[x];
+            *reinterpret_cast<u32x4 *>(dst + e * G::kPitch + p * 8) = pre[x];
         }
-        __syncthreads();
-        if (t + 1 < ntiles)
-            fetch(t + 1);
-
-        if (!active)
-            continue;
-        const int j0 = t * kTileEntries;
-        float sv = -INFINITY;
-        if (j0 < thr) {
-#pragma unroll
-            for (int st = 0; st < kTileEntries / 16; ++st) {
-                const int js = j0 + st * 16;
-                if (js < thr) {
-                    bool any = true;
-                    if (kseg) {
-                        const int jj = js + (l & 15);
-                        any = ballot(jj < thr && kseg[jj] == qseg) != 0ull;
-                    }
-                    if (any) {
-                        bf16x8 bf[KS];
-                        load_entries_lds<KS>(bf, ktile, st * 16, G::kPitch);
-                        const float s = scaled_score(subtile_score<HB, KS>(row, bf), a.scale);
-                        if ((l >> 4) == st)
-                            sv = s;
-                    }
-                }
-            }
-        }
-        const int j = j0 + l;
-        bool valid = j < thr;
-        if (valid && kseg)
-            valid = kseg[j] == qseg;
-        const float outv = valid ? sv : -INFINITY;
+    };
+    auto emit = [&](int tt, float s, bool valid) {
+        const int j = tt * kTileEntries + l;
+        const float outv = valid ? s : -INFINITY;
         if (MODE & kModeScores) {
             if (j < a.W)
                 a.scores[row_id * a.W + j] = outv;
         }
         if (MODE & kModeSelect)
             topk_push(tk, score_key(outv), (uint32_t)j, valid);
+    };
+    auto tile_valid = [&](int tt) {
+        const int j = tt * kTileEntries + l;
+        bool v = j < thr;
+        if (kseg)
+            v = v && kseg[min(j, a.W - 1)] == qseg;
+        return v;
+    };
+
+    // The first key tile's loads go out before the row operands' so the two
+    // latencies overlap.
+    if (ntiles > t_lo)
+        fetch(t_lo);
+    RowOperand<HB, KS> row;
+    if (active)
+        load_row<HB, KS>(row, a.q + b * a.q_sb + (int64_t)i * a.q_ss, a.q_sh, a.w + b * a.w_sb + (int64_t)i * a.w_ss,
+                         a.H);
+    if (ntiles > t_lo)
+        stash(t_lo & 1);
+    if (PIPE) {
+        // Software pipeline over tiles: the MFMAs of subtile 0 of tile t run
+        // alongside the epilogue of subtile 1 of tile t-1, and the MFMAs of
+        // subtile 1 alongside the epilogue of subtile 0.  Tile t-1's scores
+        // are emitted between the two halves.  The body has no data-dependent
+        // branch, so each half is one scheduling region.
+        f32x16 c0[HB], c1[HB];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+            c1[hb] = f32x16{};
+        float p0 = 0.0f;
+        bool prev_valid = false;
+        for (int t = t_lo; t < ntiles; ++t) {
+            if (t + 1 < ntiles)
+                fetch(t + 1);
+            __syncthreads();
+            if (active) {
+                const uint16_t *tile = ktile + (t & 1) * G::kTileElems;
+                const bool valid = tile_valid(t);
+                float p1;
+                {
+                    bf16x8 bf[KS];
+                    load_entries_lds<KS>(bf, tile, 0, G::kPitch);
+                    p1 = logits_with_partial<HB, KS>(c0, row, bf, c1);
+                }
+                // combined unconditionally (a lane swap), so the epilogue
+                // above stays in the MFMA region instead of sinking into the
+                // branch
+                const float prev_score = scaled_score(combine_halves(p0, p1), a.scale);
+                if (t > t_lo)
+                    emit(t - 1, prev_score, prev_valid);
+                {
+                    bf16x8 bf[KS];
+                    load_entries_lds<KS>(bf, tile, 32, G::kPitch);
+                    p0 = logits_with_partial<HB, KS>(c1, row, bf, c0);
+                }
+                prev_valid = valid;
+            }
+            if (t + 1 < ntiles)
+                stash((t + 1) & 1);
+        }
+        if (active && ntiles > t_lo)
+            emit(ntiles - 1, scaled_score(combine_halves(p0, logits_partial<HB, KS>(row, c1)), a.scale), prev_valid);
+    } else {
+        for (int t = t_lo; t < ntiles; ++t) {
+            if (t + 1 < ntiles)
+                fetch(t + 1);
+            __syncthreads();
+            if (active) {
+                const uint16_t *tile = ktile + (t & 1) * G::kTileElems;
+                const bool valid = tile_valid(t);
+                const float s = tile_scores<HB, KS>(row, true, true, a.scale, [&](bf16x8(&bf)[KS], int sub) {
+                    load_entries_lds<KS>(bf, tile, sub * 32, G::kPitch);
+                });
+                emit(t, s, valid);
+            }
+            if (t + 1 < ntiles)
+                stash((t + 1) & 1);
+        }
+    }
+    if (active && (MODE & kModeScores)) {
+        // entries before the first computed tile are masked
+        for (int j = l; j < min(t_lo * kTileEntries, a.W); j += kWave)
+            a.scores[row_id * a.W + j] = -INFINITY;
     }
 
     if (!active)
         return;
     if (MODE & kModeScores) {
-        for (int j = ntiles * kTileEntries + l; j < a.W; j += kWave)
+        for (int j = max(ntiles, t_lo) * kTileEntries + l; j < a.W; j += kWave)
             a.scores[row_id * a.W + j] = -INFINITY;
     }
     if (MODE & kModeSelect)
@@ -146,16 +243,16 @@ __global__ __launch_bounds__(kRowWaves * kWave) void rows_kernel(const KernelArg
 // ---------------------------------------------------------------------------
 // Split-row plan (long rows, few of them: decode).  Workgroup (row, chunk)
 // scores kSplitChunk consecutive entries of one row; each wave takes
-// kSplitSubtiles subtiles and reads its keys straight from HBM (every key byte
-// is used by one row only, so there is nothing to share through LDS).  Only
-// the visible prefix of the row is read.  Scores go to a.scores with row
-// stride W; with full_rows the rest of the row is filled with -inf.
+// kSplitTiles tiles of 64 entries and reads its keys straight from HBM (every
+// key byte is used by one row only, so there is nothing to share through
+// LDS).  Only the visible prefix of the row is read.  Scores go to a.scores
+// with row stride W; with full_rows the rest of the row is filled with -inf.
 // ---------------------------------------------------------------------------
 template <int D, int HB>
 __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(const KernelArgs a)
 {
-    constexpr int KS = D / 32;
-    constexpr int kWaveEntries = kSplitSubtiles * 16;
+    constexpr int KS = D / 16;
+    constexpr int kWaveEntries = kSplitTiles * kTileEntries;
     const int wv = threadIdx.x / kWave;
     const int l = lane();
     const int64_t row_id = blockIdx.x / a.n_chunks;
@@ -180,71 +277,116 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(const Kernel
     const uint16_t *kb = a.k + b * a.k_sb;
 
 #pragma unroll 1
-    for (int g4 = 0; g4 < kSplitSubtiles / 4; ++g4) {
-        const int j0 = base + g4 * 64;
+    for (int t = 0; t < kSplitTiles; ++t) {
+        const int j0 = base + t * kTileEntries;
         if (j0 >= thr && !a.full_rows)
             break;
-        float sv = -INFINITY;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int js = j0 + st * 16;
-            if (js < thr) {
-                bool any = true;
-                if (kseg) {
-                    const int jj = js + (l & 15);
-                    any = ballot(jj < thr && kseg[jj] == qseg) != 0ull;
-                }
-                if (any) {
-                    bf16x8 bf[KS];
-                    load_entries_global<KS>(bf, kb, a.k_sw, js, thr);
-                    const float s = scaled_score(subtile_score<HB, KS>(row, bf), a.scale);
-                    if ((l >> 4) == st)
-                        sv = s;
-                }
-            }
-        }
         const int j = j0 + l;
         bool valid = j < thr;
-        if (valid && kseg)
-            valid = kseg[j] == qseg;
+        if (kseg)
+            valid = valid && kseg[j] == qseg;
+        bool do0, do1;
+        if (kseg) {
+            const uint64_t bal = ballot(valid);
+            do0 = (uint32_t)bal != 0u;
+            do1 = (uint32_t)(bal >> 32) != 0u;
+        } else {
+            do0 = j0 < thr;
+            do1 = j0 + 32 < thr;
+        }
+        float s = -INFINITY;
+        if (do0 || do1)
+            s = tile_scores<HB, KS>(row, do0, do1, a.scale, [&](bf16x8(&bf)[KS], int sub) {
+                load_entries_global<KS>(bf, kb, a.k_sw, j0 + sub * 32, thr);
+            });
         if (j < a.W && (a.full_rows || j < thr))
-            out[j] = valid ? sv : -INFINITY;
+            out[j] = valid ? s : -INFINITY;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Row top-k over a dense fp32 score matrix: one wave per row streams the row
-// through a TopKRow buffer.  With limit_rows the row ends at its visible
-// prefix (used after the split plan, whose rows are only written that far).
+// Row top-k over a dense fp32 score matrix, one wave per row (short rows).
+// With limit_rows the row ends at its visible prefix (q_offset, m).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int row_length(const KernelArgs &a, int64_t row)
+{
+    if (!a.limit_rows)
+        return a.W;
+    const int b = (int)(row / a.S), i = (int)(row % a.S);
+    const int64_t off = a.q_offset ? (int64_t)a.q_offset[b] : 0;
+    return visible_entries(off + i, a.m, a.W);
+}
+
+// Stream src[j0 .. j1) (j1 - j0 a multiple of 64 or the row end n) into the
+// wave's buffer, eight 64-entry chunks per batch of loads.
+__device__ __forceinline__ void stream_row(TopKRow &tk, const float *src, int j0, int j1, int n)
+{
+    const int l = lane();
+    constexpr int kBatch = 8;
+#pragma unroll 1
+    for (int base = j0; base < j1; base += kBatch * kWave) {
+        float v[kBatch];
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c) {
+            const int j = base + c * kWave + l;
+            v[c] = src[min(j, n - 1)];
+        }
+#pragma unroll
+        for (int c = 0; c < kBatch; ++c) {
+            const int j = base + c * kWave + l;
+            const bool in = j < j1;
+            const uint32_t kv = score_key(v[c]);
+            topk_push(tk, kv, (uint32_t)j, in && key_selectable(kv));
+        }
+    }
+}
+
 __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(const KernelArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int wv = threadIdx.x / kWave;
-    const int l = lane();
     const int64_t row = (int64_t)blockIdx.x * kTopkWaves + wv;
     if (row >= a.rows)
         return;
-    int n = a.W;
-    if (a.limit_rows) {
-        const int b = (int)(row / a.S), i = (int)(row % a.S);
-        const int64_t off = a.q_offset ? (int64_t)a.q_offset[b] : 0;
-        n = visible_entries(off + i, a.m, a.W);
-    }
+    const int n = row_length(a, row);
     unsigned char *base = smem + (size_t)wv * (1024 + (size_t)a.cap * 8);
     uint32_t *hist = reinterpret_cast<uint32_t *>(base);
     uint32_t *key = hist + 256;
     TopKRow tk;
     topk_init(tk, key, key + a.cap, hist, a.cap, a.top_k);
-    const float *src = a.scores + row * a.W;
-#pragma unroll 1
-    for (int j0 = 0; j0 < n; j0 += kWave) {
-        const int j = j0 + l;
-        const float s = (j < n) ? src[j] : -INFINITY;
-        const uint32_t kv = score_key(s);
-        topk_push(tk, kv, (uint32_t)j, j < n && key_selectable(kv));
-    }
+    if (n > 0)
+        stream_row(tk, a.scores + row * a.W, 0, n, n);
     topk_finish(tk, a.idx + row * a.top_k);
+}
+
+// ---------------------------------------------------------------------------
+// Row top-k for long rows: one workgroup per row; wave w streams the w-th
+// contiguous segment into its own buffer, then the waves select jointly.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(const KernelArgs a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int wv = threadIdx.x / kWave;
+    const int64_t row = blockIdx.x;
+    const int n = row_length(a, row);
+    uint32_t *hist_all = reinterpret_cast<uint32_t *>(smem);            // [kTopkBlockWaves][256]
+    uint32_t *keys = hist_all + kTopkBlockWaves * 256;                  // [kTopkBlockWaves][cap]
+    uint32_t *ents = keys + (size_t)kTopkBlockWaves * a.cap;            // [kTopkBlockWaves][cap]
+    int *cnt = reinterpret_cast<int *>(ents + (size_t)kTopkBlockWaves * a.cap);  // [kTopkBlockWaves + 2]
+    uint32_t *sel_key = reinterpret_cast<uint32_t *>(cnt + kTopkBlockWaves + 2);  // [top_k]
+    uint32_t *sel_ent = sel_key + a.top_k;                              // [top_k]
+
+    // segments of whole 64-entry chunks
+    const int chunks = (n + kWave - 1) / kWave;
+    const int per = (chunks + kTopkBlockWaves - 1) / kTopkBlockWaves;
+    const int j0 = min(wv * per * kWave, n), j1 = min((wv + 1) * per * kWave, n);
+    TopKRow tk;
+    topk_init(tk, keys + (size_t)wv * a.cap, ents + (size_t)wv * a.cap, hist_all + wv * 256, a.cap, a.top_k);
+    if (j1 > j0)
+        stream_row(tk, a.scores + row * a.W, j0, j1, n);
+    topk_reduce(tk);
+    block_select_sort<kTopkBlockWaves>(keys, ents, a.cap, tk.count, a.top_k, hist_all, cnt, sel_key, sel_ent,
+                                       a.idx + row * a.top_k);
 }
 
 // ---------------------------------------------------------------------------
@@ -252,12 +394,17 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(const KernelAr
 // ---------------------------------------------------------------------------
 size_t rows_lds_bytes(int D, int mode, int cap)
 {
-    size_t tile = (size_t)kTileEntries * (D + 8) * 2;
+    size_t tile = 2 * (size_t)kTileEntries * (D + 8) * 2;
     size_t sel = (mode & kModeSelect) ? (size_t)kRowWaves * (1024 + (size_t)cap * 8) : 0;
     return tile + sel;
 }
 
 size_t topk_lds_bytes(int cap) { return (size_t)kTopkWaves * (1024 + (size_t)cap * 8); }
+
+size_t topk_block_lds_bytes(int cap, int top_k)
+{
+    return (size_t)kTopkBlockWaves * (1024 + (size_t)cap * 8) + (kTopkBlockWaves + 2) * 4 + (size_t)top_k * 8;
+}
 
 template <typename K>
 static hipError_t launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, const KernelArgs &a)
@@ -295,7 +442,6 @@ static hipError_t launch_rows_d(int HB, int mode, const KernelArgs &a, size_t ld
     case 1: return launch_rows_t<D, 1>(mode, a, lds, s);
     case 2: return launch_rows_t<D, 2>(mode, a, lds, s);
     case 4: return launch_rows_t<D, 4>(mode, a, lds, s);
-    case 8: return launch_rows_t<D, 8>(mode, a, lds, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -318,7 +464,6 @@ static hipError_t launch_split_d(int HB, const KernelArgs &a, hipStream_t s)
     case 1: return launch(split_kernel<D, 1>, grid, block, 0, s, a);
     case 2: return launch(split_kernel<D, 2>, grid, block, 0, s, a);
     case 4: return launch(split_kernel<D, 4>, grid, block, 0, s, a);
-    case 8: return launch(split_kernel<D, 8>, grid, block, 0, s, a);
     default: return hipErrorInvalidValue;
     }
 }
@@ -337,6 +482,12 @@ hipError_t launch_topk(const KernelArgs &a, size_t lds, hipStream_t s)
 {
     dim3 grid((unsigned)((a.rows + kTopkWaves - 1) / kTopkWaves)), block(kTopkWaves * kWave);
     return launch(topk_kernel, grid, block, lds, s, a);
+}
+
+hipError_t launch_topk_block(const KernelArgs &a, size_t lds, hipStream_t s)
+{
+    dim3 grid((unsigned)a.rows), block(kTopkBlockWaves * kWave);
+    return launch(topk_block_kernel, grid, block, lds, s, a);
 }
 
 } // namespace csa

@@ -36,10 +36,13 @@ constexpr int kRowsPerBlock = kRowWaves;
 constexpr int kTileEntries = 64;        // compressed entries per LDS K tile
 // Split plan geometry.
 constexpr int kSplitWaves = 4;
-constexpr int kSplitSubtiles = 16;      // 16-entry subtiles per wave
-constexpr int kSplitChunk = kSplitWaves * kSplitSubtiles * 16;
-// Top-k kernel geometry.
+constexpr int kSplitTiles = 4;          // 64-entry tiles per wave
+constexpr int kSplitChunk = kSplitWaves * kSplitTiles * kTileEntries;
+// Top-k kernel geometry: one wave per row, or one workgroup per long row.
 constexpr int kTopkWaves = 4;
+constexpr int kTopkBlockWaves = 8;
+// Rows at least this long use the workgroup-per-row top-k.
+constexpr int kTopkBlockMinLen = 8192;
 
 enum { kModeScores = 1, kModeSelect = 2 };
 
@@ -49,10 +52,12 @@ __host__ __device__ constexpr int topk_capacity(int k) { return ((k + 63) / 64) 
 
 size_t rows_lds_bytes(int D, int mode, int cap);
 size_t topk_lds_bytes(int cap);
+size_t topk_block_lds_bytes(int cap, int top_k);
 
 // Each returns hipSuccess or the launch error; nothing is synchronised.
 hipError_t launch_rows(int D, int HB, int mode, const KernelArgs &a, size_t lds, hipStream_t s);
 hipError_t launch_split(int D, int HB, const KernelArgs &a, hipStream_t s);
 hipError_t launch_topk(const KernelArgs &a, size_t lds, hipStream_t s);
+hipError_t launch_topk_block(const KernelArgs &a, size_t lds, hipStream_t s);
 
 } // namespace csa

@@ -1,100 +1,213 @@
-// The indexer score of one query row against 16 compressed entries, on MFMA.
+// The indexer score of one query row against a tile of 64 compressed
+// entries, on MFMA.
 //
 // For query row i the heads are the MFMA M dimension and the entries the N
-// dimension: D(16 heads x 16 entries) = Q_i(16 heads x 32 of D) * K^T(32 of D x
-// 16 entries), accumulated over D in fp32.  Each lane then holds 4 heads of
-// one entry, so the ReLU and the head-weighted sum run in registers
-// (max + fma per head), and two cross-lane adds finish the sum over heads.
-// The per-head logits never leave the register file.
+// dimension: D(32 heads x 32 entries) = Q_i(32 heads x 16 of D) * K^T(16 of D x
+// 32 entries), accumulated over D in fp32 (v_mfma_f32_32x32x16_bf16, the
+// full-rate bf16 MFMA on gfx950).  Each lane then holds 16 heads of one entry,
+// so the ReLU and the head-weighted sum run in registers (integer max + fma
+// per head), and one cross-half lane swap per 64 entries finishes the sum over
+// heads.  The per-head logits never leave the register file.
 //
-// Every kernel calls subtile_score(), so every plan yields the same fp32 bits.
+// Every kernel computes scores through tile_scores(), so every plan yields
+// the same fp32 bits.
 #pragma once
 
 #include "csa_device.hpp"
 
 namespace csa {
 
-// One query row resident in registers: A fragments of every 16-head block and
-// k-step, plus this lane's head weights (heads 16*hb + 4*(lane/16) + r).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.  Lane l
+// supplies A row (l % 32), B column (l % 32) and eight consecutive k values
+// selected by l / 32; it receives D column (l % 32), rows
+// 8*(r/4) + 4*(l/32) + (r%4) for r = 0..15.  A and B use the same k
+// assignment, so any consistent placement of the contraction index inside a
+// fragment yields the same dot products.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Head of accumulator register r in lane group g (= lane / 32) of a 32-head block.
+__host__ __device__ constexpr int c_row(int r, int g) { return 8 * (r / 4) + 4 * g + (r % 4); }
+
+// ReLU on fp32 through the integer max: every negative float (and -0) has a
+// negative int32 image, so max(bits, 0) is +0 for them and the identity for
+// positive values.  One VALU op, exact.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// One query row resident in registers: A fragments of every 32-head block and
+// 16-wide k-step, plus this lane's head weights (heads 32*hb + c_row(r, lane/32)).
 template <int HB, int KS>
 struct RowOperand {
     bf16x8 a[HB][KS];
-    float w[HB][4];
+    float w[HB][16];
 };
 
-// q_row = q + b*q_sb + i*q_ss, w_row = w + b*w_sb + i*w_ss.  Heads >= H read
-// as zero queries with zero weight, which adds exact zeros.
+// q_row = q + b*q_sb + i*q_ss, w_row = w + b*w_sb + i*w_ss.  Heads >= H get
+// weight zero and the (finite) queries of head H-1, so they add exact zeros.
+// Loads are issued unconditionally from clamped addresses so they can all be
+// in flight at once.
+// With full head blocks (H == 32*HB) no padding is applied, so nothing
+// consumes the loaded values before the first tile: the loads stay in flight
+// while the workgroup stages its first key tile.
 template <int HB, int KS>
 __device__ __forceinline__ void load_row(RowOperand<HB, KS> &r, const uint16_t *q_row, int64_t q_sh,
                                          const uint16_t *w_row, int H)
 {
     const int l = lane();
-    const int n = l & 15, g = l >> 4;
+    const int n = l & 31, g = l >> 5;
+    const bool full = H == 32 * HB;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
-        const int h = hb * 16 + n;
+        const int h = hb * 32 + n;
+        const uint16_t *p = q_row + (int64_t)min(h, H - 1) * q_sh + 8 * g;
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-            r.a[hb][s] = (h < H) ? load_frag(q_row + (int64_t)h * q_sh + s * 32 + 8 * g) : zero_frag();
+            r.a[hb][s] = load_frag(p + 16 * s);
     }
+    uint16_t wb[HB][16];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int h = hb * 16 + 4 * g + rr;
-            r.w[hb][rr] = (h < H) ? bf16_to_f32(w_row[h]) : 0.0f;
-        }
+        for (int rr = 0; rr < 16; ++rr)
+            wb[hb][rr] = w_row[min(hb * 32 + c_row(rr, g), H - 1)];
+    if (full) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr)
+                r.w[hb][rr] = bf16_to_f32(wb[hb][rr]);
+    } else {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr)
+                r.w[hb][rr] = (hb * 32 + c_row(rr, g) < H) ? bf16_to_f32(wb[hb][rr]) : 0.0f;
+    }
 }
 
-// B fragments of 16 entries staged in LDS with a row pitch of `pitch`
-// elements: lane l reads entry (l % 16), 8 values at 32*s + 8*(l/16).
+// B fragments of 32 entries staged in LDS with a row pitch of `pitch`
+// elements: lane l reads entry (l % 32), 8 values at 16*s + 8*(l/32).
 template <int KS>
 __device__ __forceinline__ void load_entries_lds(bf16x8 (&b)[KS], const uint16_t *tile, int entry0, int pitch)
 {
     const int l = lane();
-    const uint16_t *p = tile + (entry0 + (l & 15)) * pitch + 8 * (l >> 4);
+    const uint16_t *p = tile + (entry0 + (l & 31)) * pitch + 8 * (l >> 5);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-        b[s] = load_frag(p + 32 * s);
+        b[s] = load_frag(p + 16 * s);
 }
 
-// B fragments straight from global memory; entries at or beyond `limit`
-// are not read (zero fragments).
+// B fragments straight from global memory.  Entries at or beyond `limit`
+// (always masked by the caller) are not read: those lanes read entry
+// entry0 instead, which is below the limit.
 template <int KS>
 __device__ __forceinline__ void load_entries_global(bf16x8 (&b)[KS], const uint16_t *k_batch, int64_t k_sw,
                                                     int entry0, int limit)
 {
     const int l = lane();
-    const int j = entry0 + (l & 15);
-    const uint16_t *p = k_batch + (int64_t)j * k_sw + 8 * (l >> 4);
+    int j = entry0 + (l & 31);
+    j = j < limit ? j : entry0;
+    const uint16_t *p = k_batch + (int64_t)j * k_sw + 8 * (l >> 5);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-        b[s] = (j < limit) ? load_frag(p + 32 * s) : zero_frag();
+        b[s] = load_frag(p + 16 * s);
 }
 
-// Unscaled score sum_h w_h * ReLU(q_h . k_j) of entry (lane % 16); the four
-// lane groups return the same bits.
+// Per-head logits of 32 entries: c[hb] = Q(heads 32hb..32hb+31) . K^T.
 template <int HB, int KS>
-__device__ __forceinline__ float subtile_score(const RowOperand<HB, KS> &r, const bf16x8 (&b)[KS])
+__device__ __forceinline__ void subtile_logits(f32x16 (&c)[HB], const RowOperand<HB, KS> &r, const bf16x8 (&b)[KS])
 {
-    f32x4 c[HB];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
-        c[hb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        c[hb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
-            c[hb] = mfma16(r.a[hb][s], b[s], c[hb]);
-    float acc = 0.0f;
+            c[hb] = mfma32(r.a[hb][s], b[s], c[hb]);
+}
+
+// This lane's share of the unscaled score of entry (lane % 32): the sum over
+// its 16 heads of every 32-head block, w_h * ReLU(logit_h).  Each head block
+// has its own fma chain; the chains are added in a fixed order.
+template <int HB, int KS>
+__device__ __forceinline__ float logits_partial(const RowOperand<HB, KS> &r, const f32x16 (&c)[HB])
+{
+    float acc[HB];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
+    for (int hb = 0; hb < HB; ++hb) {
+        acc[hb] = 0.0f;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            acc = __builtin_fmaf(r.w[hb][rr], fmaxf(c[hb][rr], 0.0f), acc);
-    acc += __shfl_xor(acc, 16, kWave);
-    acc += __shfl_xor(acc, 32, kWave);
-    return acc;
+        for (int rr = 0; rr < 16; ++rr)
+            acc[hb] = __builtin_fmaf(r.w[hb][rr], relu(c[hb][rr]), acc[hb]);
+    }
+#pragma unroll
+    for (int step = 1; step < HB; step <<= 1)
+#pragma unroll
+        for (int hb = 0; hb + step < HB; hb += 2 * step)
+            acc[hb] += acc[hb + step];
+    return acc[0];
+}
+
+template <int HB, int KS>
+__device__ __forceinline__ float subtile_partial(const RowOperand<HB, KS> &r, const bf16x8 (&b)[KS])
+{
+    f32x16 c[HB];
+    subtile_logits<HB, KS>(c, r, b);
+    return logits_partial<HB, KS>(r, c);
+}
+
+// Logits of one subtile (into cnew, from zero) and the partial of another
+// subtile whose logits are cold, interleaved in program order: every k-step
+// issues one MFMA per head block (independent accumulators, so no MFMA waits
+// on the previous one) followed by its share of the cold subtile's
+// max + fma work, which runs while the matrix core is busy.  Scheduling
+// fences keep that order.  The fma chains visit heads in the same order as
+// logits_partial(), so the partial is bit-identical to it.
+template <int HB, int KS>
+__device__ __forceinline__ float logits_with_partial(f32x16 (&cnew)[HB], const RowOperand<HB, KS> &r,
+                                                     const bf16x8 (&b)[KS], const f32x16 (&cold)[HB])
+{
+    static_assert((HB * 16) % KS == 0, "epilogue must split evenly over the k-steps");
+    constexpr int kPer = HB * 16 / KS;
+    float acc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        cnew[hb] = f32x16{};
+        acc[hb] = 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+            cnew[hb] = mfma32(r.a[hb][s], b[s], cnew[hb]);
+#pragma unroll
+        for (int p = 0; p < kPer; ++p) {
+            const int idx = s * kPer + p, hb = idx / 16, rr = idx % 16;
+            acc[hb] = __builtin_fmaf(r.w[hb][rr], relu(cold[hb][rr]), acc[hb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int step = 1; step < HB; step <<= 1)
+#pragma unroll
+        for (int hb = 0; hb + step < HB; hb += 2 * step)
+            acc[hb] += acc[hb + step];
+    return acc[0];
+}
+
+// Combine the lane shares of two 32-entry subtiles (entries j0..j0+31 in p0,
+// j0+32..j0+63 in p1): after one swap of lane halves, lane l holds the full
+// unscaled score of entry j0 + l (its own half's share plus the other half's,
+// low half first).
+__device__ __forceinline__ float combine_halves(float p0, float p1)
+{
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 // Apply the scale once and turn a -0 result into +0.

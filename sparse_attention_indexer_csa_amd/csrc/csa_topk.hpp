@@ -1,14 +1,20 @@
-// Exact per-row top-k, run by one wave over a stream of (key, entry) pairs that
-// arrive in increasing entry order, 64 at a time.
+// Exact per-row top-k.
 //
-// The wave keeps a candidate buffer of `cap` pairs in LDS and a threshold
-// tau: a pair may enter only if its key is > tau.  When the buffer would
-// overflow, a radix select finds T, the k-th largest key in the buffer, and an
-// order-preserving compaction keeps every key > T plus the earliest keys == T
-// up to k pairs; tau becomes T.  A later pair with key <= T can never make the
-// top k: k kept pairs beat it (larger key, or equal key and lower entry).  At
-// the end the same select leaves exactly min(k, count) pairs, which a bitonic
-// sort orders by (key descending, entry ascending).
+// Wave level (TopKRow): one wave owns a row and receives its (key, entry)
+// pairs 64 at a time in increasing entry order.  It keeps a candidate buffer
+// of `cap` pairs in LDS and a threshold tau: a pair may enter only if its key
+// is > tau.  When the buffer would overflow, a radix select finds T, the k-th
+// largest key in the buffer, and an order-preserving compaction keeps every
+// key > T plus the earliest keys == T, k pairs in all; tau becomes T.  A later
+// pair with key <= T can never make the top k: k kept pairs beat it (larger
+// key, or equal key and lower entry).  At the end the same select leaves
+// exactly min(k, count) pairs, which a bitonic sort orders by (key
+// descending, entry ascending).
+//
+// Block level (block_select_sort): several waves that each hold a candidate
+// buffer for a contiguous segment of one row (segments in increasing entry
+// order) run one shared radix select over the union, keep the winners in
+// entry order, and one wave sorts them.
 //
 // Keys are score_key() images of fp32 scores, so key order is score order and
 // -0 ties with +0.
@@ -20,13 +26,13 @@
 namespace csa {
 
 struct TopKRow {
-    uint32_t *key; // LDS [cap]
-    uint32_t *ent; // LDS [cap]
+    uint32_t *key;  // LDS [cap]
+    uint32_t *ent;  // LDS [cap]
     uint32_t *hist; // LDS [256], scratch of the owning wave
-    int cap;       // >= k + 64
+    int cap;        // >= k + 64
     int k;
-    int count;     // wave-uniform
-    uint32_t tau;  // wave-uniform
+    int count;      // wave-uniform
+    uint32_t tau;   // wave-uniform
 };
 
 __device__ __forceinline__ void topk_init(TopKRow &t, uint32_t *key, uint32_t *ent, uint32_t *hist, int cap, int k)
@@ -40,6 +46,36 @@ __device__ __forceinline__ void topk_init(TopKRow &t, uint32_t *key, uint32_t *e
     t.tau = kKeyNegInf;
 }
 
+// Digit search shared by the wave and block selects: hist holds 256 counts
+// of the current digit; find the digit d such that fewer than kk keys lie in
+// higher digits and at least kk in digits >= d.  Returns d; `above` receives
+// the count in higher digits.  Run by one whole wave.
+__device__ __forceinline__ int find_digit(const uint32_t *hist, int kk, int &above)
+{
+    const int l = lane();
+    // lane l owns digits 255-4l, 254-4l, 253-4l, 252-4l (descending)
+    int h[4], tot = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        h[r] = (int)hist[255 - 4 * l - r];
+        tot += h[r];
+    }
+    int cum = wave_exclusive_sum(tot);
+    int found = -1, ab = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (found < 0 && cum < kk && kk <= cum + h[r]) {
+            found = 255 - 4 * l - r;
+            ab = cum;
+        }
+        cum += h[r];
+    }
+    const uint64_t bal = ballot(found >= 0);
+    const int src = bal ? (int)__builtin_ctzll(bal) : 0;
+    above = read_lane(ab, src);
+    return read_lane(found, src) & 0xFF;
+}
+
 // Radix select over key[0..count), count > k: the k-th largest key T, and how
 // many keys equal to T belong to the top k (the earliest ones in buffer order).
 __device__ __forceinline__ void radix_select(const uint32_t *key, int count, int k, uint32_t *hist, uint32_t &T,
@@ -48,6 +84,7 @@ __device__ __forceinline__ void radix_select(const uint32_t *key, int count, int
     const int l = lane();
     uint32_t prefix = 0u, mask = 0u;
     int kk = k;
+    wave_lds_fence();
 #pragma unroll 1
     for (int shift = 24; shift >= 0; shift -= 8) {
         for (int bin = l; bin < 256; bin += kWave)
@@ -59,28 +96,10 @@ __device__ __forceinline__ void radix_select(const uint32_t *key, int count, int
                 atomicAdd(&hist[(kv >> shift) & 0xFFu], 1u);
         }
         wave_lds_fence();
-        // lane l owns bins 255-4l, 254-4l, 253-4l, 252-4l (descending).
-        int h[4], tot = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            h[r] = (int)hist[255 - 4 * l - r];
-            tot += h[r];
-        }
-        int cum = wave_exclusive_sum(tot);
-        int found = -1, above = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (found < 0 && cum < kk && kk <= cum + h[r]) {
-                found = 255 - 4 * l - r;
-                above = cum;
-            }
-            cum += h[r];
-        }
-        const uint64_t bal = ballot(found >= 0);
-        const int src = bal ? (int)__builtin_ctzll(bal) : 0;
-        const int digit = read_lane(found, src);
-        kk -= read_lane(above, src);
-        prefix |= (uint32_t)(digit & 0xFF) << shift;
+        int above;
+        const int digit = find_digit(hist, kk, above);
+        kk -= above;
+        prefix |= (uint32_t)digit << shift;
         mask |= 0xFFu << shift;
         wave_lds_fence();
     }
@@ -115,18 +134,27 @@ __device__ __forceinline__ int compact_keep(uint32_t *key, uint32_t *ent, int co
     return out;
 }
 
-// Offer one pair per lane; lanes must hold increasing entries.
+// Reduce the buffer to its top k (no-op when it holds at most k pairs).
+__device__ __forceinline__ void topk_reduce(TopKRow &t)
+{
+    if (t.count > t.k) {
+        uint32_t T;
+        int keep;
+        radix_select(t.key, t.count, t.k, t.hist, T, keep);
+        t.count = uniform(compact_keep(t.key, t.ent, t.count, T, keep));
+        t.tau = uniform_u(T);
+    }
+}
+
+// Offer one pair per lane; lanes must hold increasing entries, and every pair
+// offered later must have a larger entry.
 __device__ __forceinline__ void topk_push(TopKRow &t, uint32_t kv, uint32_t entry, bool valid)
 {
     bool pass = valid && kv > t.tau;
     uint64_t bal = ballot(pass);
     int n = popc64(bal);
     if (t.count + n > t.cap) {
-        uint32_t T;
-        int keep;
-        radix_select(t.key, t.count, t.k, t.hist, T, keep);
-        t.count = uniform(compact_keep(t.key, t.ent, t.count, T, keep));
-        t.tau = uniform_u(T);
+        topk_reduce(t);
         pass = valid && kv > t.tau;
         bal = ballot(pass);
         n = popc64(bal);
@@ -137,10 +165,53 @@ __device__ __forceinline__ void topk_push(TopKRow &t, uint32_t kv, uint32_t entr
         t.ent[pos] = entry;
     }
     t.count += n;
-    wave_lds_fence();
 }
 
-// In-register stages (partner in the same lane) of one bitonic merge level.
+// ---------------------------------------------------------------------------
+// Bitonic sort of 64*E values held by one wave, lane l holding elements
+// l*E .. l*E+E-1, into descending order.  Partners at lane distance 1, 2 and
+// 8 are fetched with DPP, 4 and 16 with a swizzle, 32 with the gfx950 lane
+// swap; partners inside a lane are plain registers.
+// ---------------------------------------------------------------------------
+template <int LX>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v)
+{
+    if constexpr (LX == 1)
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false); // quad_perm [1,0,3,2]
+    else if constexpr (LX == 2)
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false); // quad_perm [2,3,0,1]
+    else if constexpr (LX == 8)
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false); // row_ror:8
+    else if constexpr (LX == 4)
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F); // xor 4 within 32 lanes
+    else if constexpr (LX == 16)
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F); // xor 16 within 32 lanes
+    else {
+        // lane distance 32: swap the halves (v itself gives the other half)
+        const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane() < 32) ? sw[1] : sw[0];
+    }
+}
+
+// One cross-lane stage: partners at lane distance LX.  For these stages the
+// keep-larger flag depends only on the lane (stride and size are multiples
+// of E), so it is computed once.
+template <int LX, int E>
+__device__ __forceinline__ void cross_stage(uint64_t (&v)[E], bool keep_max)
+{
+    uint32_t ohi[E], olo[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        ohi[r] = lane_xor_u32<LX>((uint32_t)(v[r] >> 32));
+        olo[r] = lane_xor_u32<LX>((uint32_t)v[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const uint64_t o = ((uint64_t)ohi[r] << 32) | olo[r];
+        v[r] = ((v[r] > o) == keep_max) ? v[r] : o;
+    }
+}
+
 template <int E>
 __device__ __forceinline__ void bitonic_in_lane(uint64_t (&v)[E], int size, int l)
 {
@@ -150,8 +221,7 @@ __device__ __forceinline__ void bitonic_in_lane(uint64_t (&v)[E], int size, int 
 #pragma unroll
             for (int r = 0; r < E; ++r) {
                 if ((r & stride) == 0) {
-                    const int e = l * E + r;
-                    const bool desc = (e & size) == 0;
+                    const bool desc = ((l * E + r) & size) == 0;
                     const uint64_t a = v[r], b = v[r + stride];
                     const bool sw = desc ? (a < b) : (a > b);
                     v[r] = sw ? b : a;
@@ -162,8 +232,6 @@ __device__ __forceinline__ void bitonic_in_lane(uint64_t (&v)[E], int size, int 
     }
 }
 
-// Sort the 64*E values held by the wave (lane l holds elements l*E .. l*E+E-1)
-// in descending order.
 template <int E>
 __device__ __forceinline__ void bitonic_sort_desc(uint64_t (&v)[E])
 {
@@ -172,22 +240,22 @@ __device__ __forceinline__ void bitonic_sort_desc(uint64_t (&v)[E])
     for (int size = 2; size <= kWave * E; size <<= 1) {
 #pragma unroll 1
         for (int stride = size >> 1; stride >= E; stride >>= 1) {
-            const int lx = stride / E;
-#pragma unroll
-            for (int r = 0; r < E; ++r) {
-                const int e = l * E + r;
-                const uint64_t o = shfl_xor_u64(v[r], lx);
-                const bool keep_max = ((e & stride) == 0) == ((e & size) == 0);
-                const uint64_t mx = v[r] > o ? v[r] : o;
-                const uint64_t mn = v[r] > o ? o : v[r];
-                v[r] = keep_max ? mx : mn;
+            const int e = l * E;
+            const bool keep_max = ((e & stride) == 0) == ((e & size) == 0);
+            switch (stride / E) {
+            case 1: cross_stage<1, E>(v, keep_max); break;
+            case 2: cross_stage<2, E>(v, keep_max); break;
+            case 4: cross_stage<4, E>(v, keep_max); break;
+            case 8: cross_stage<8, E>(v, keep_max); break;
+            case 16: cross_stage<16, E>(v, keep_max); break;
+            default: cross_stage<32, E>(v, keep_max); break;
             }
         }
         bitonic_in_lane<E>(v, size, l);
     }
 }
 
-// Sort the n selected pairs and write out[0..k): entries, then -1 padding.
+// Sort the n pairs key/ent[0..n) and write out[0..k): entries, then -1.
 template <int E>
 __device__ __forceinline__ void sort_and_write(const uint32_t *key, const uint32_t *ent, int n, int k, int32_t *out)
 {
@@ -210,28 +278,137 @@ __device__ __forceinline__ void sort_and_write(const uint32_t *key, const uint32
         out[e] = -1;
 }
 
+__device__ __forceinline__ void sort_pairs_and_write(const uint32_t *key, const uint32_t *ent, int n, int k,
+                                                     int32_t *out)
+{
+    wave_lds_fence();
+    if (n <= 64)
+        sort_and_write<1>(key, ent, n, k, out);
+    else if (n <= 128)
+        sort_and_write<2>(key, ent, n, k, out);
+    else if (n <= 256)
+        sort_and_write<4>(key, ent, n, k, out);
+    else if (n <= 512)
+        sort_and_write<8>(key, ent, n, k, out);
+    else if (n <= 1024)
+        sort_and_write<16>(key, ent, n, k, out);
+    else
+        sort_and_write<32>(key, ent, n, k, out);
+}
+
 // Final selection of the row into out[0..k) (global memory).
 __device__ __forceinline__ void topk_finish(TopKRow &t, int32_t *out)
 {
-    int n = t.count;
-    if (n > t.k) {
-        uint32_t T;
-        int keep;
-        radix_select(t.key, n, t.k, t.hist, T, keep);
-        n = uniform(compact_keep(t.key, t.ent, n, T, keep));
+    topk_reduce(t);
+    sort_pairs_and_write(t.key, t.ent, t.count, t.k, out);
+}
+
+// ---------------------------------------------------------------------------
+// Block-level finish.  Wave w of NW holds key/ent[w*cap .. w*cap + cnt[w]) in
+// LDS, each already reduced to at most k pairs, segments in entry order.  All
+// NW waves of the workgroup call this together.  `hist` is 256 shared words,
+// `cnt` NW+2 shared words, `sel_key`/`sel_ent` k shared words each.
+// ---------------------------------------------------------------------------
+template <int NW>
+__device__ __forceinline__ void block_select_sort(uint32_t *key, uint32_t *ent, int cap, int my_count, int k,
+                                                  uint32_t *hist, int *cnt, uint32_t *sel_key, uint32_t *sel_ent,
+                                                  int32_t *out)
+{
+    const int wv = threadIdx.x / kWave, l = lane();
+    uint32_t *mk = key + wv * cap;
+    uint32_t *me = ent + wv * cap;
+    if (l == 0)
+        cnt[wv] = my_count;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        total += cnt[w];
+
+    uint32_t T = 0u;
+    int kk = 0;
+    const bool select = total > k;
+    if (select) {
+        uint32_t prefix = 0u, mask = 0u;
+        kk = k;
+#pragma unroll 1
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int b = threadIdx.x; b < 256; b += NW * kWave)
+                hist[b] = 0u;
+            __syncthreads();
+            for (int i = l; i < my_count; i += kWave) {
+                const uint32_t kv = mk[i];
+                if ((kv & mask) == prefix)
+                    atomicAdd(&hist[(kv >> shift) & 0xFFu], 1u);
+            }
+            __syncthreads();
+            if (wv == 0) {
+                int above;
+                const int digit = find_digit(hist, kk, above);
+                if (l == 0) {
+                    cnt[NW] = digit;
+                    cnt[NW + 1] = above;
+                }
+            }
+            __syncthreads();
+            kk -= cnt[NW + 1];
+            prefix |= (uint32_t)cnt[NW] << shift;
+            mask |= 0xFFu << shift;
+            __syncthreads();
+        }
+        T = prefix;
     }
-    if (n <= 64)
-        sort_and_write<1>(t.key, t.ent, n, t.k, out);
-    else if (n <= 128)
-        sort_and_write<2>(t.key, t.ent, n, t.k, out);
-    else if (n <= 256)
-        sort_and_write<4>(t.key, t.ent, n, t.k, out);
-    else if (n <= 512)
-        sort_and_write<8>(t.key, t.ent, n, t.k, out);
-    else if (n <= 1024)
-        sort_and_write<16>(t.key, t.ent, n, t.k, out);
-    else
-        sort_and_write<32>(t.key, t.ent, n, t.k, out);
+    // per-wave counts of winners above T and of ties, for ordered placement
+    int gt = 0, eq = 0;
+    for (int i = l; i < my_count; i += kWave) {
+        const uint32_t kv = mk[i];
+        gt += (!select || kv > T) ? 1 : 0;
+        eq += (select && kv == T) ? 1 : 0;
+    }
+    gt = wave_exclusive_sum(gt) + gt; // inclusive: last lane has the wave total
+    eq = wave_exclusive_sum(eq) + eq;
+    if (l == kWave - 1) {
+        hist[wv] = (uint32_t)gt;
+        hist[NW + wv] = (uint32_t)eq;
+    }
+    __syncthreads();
+    int gt_before = 0, eq_before = 0, gt_total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        gt_before += (w < wv) ? (int)hist[w] : 0;
+        eq_before += (w < wv) ? (int)hist[NW + w] : 0;
+        gt_total += (int)hist[w];
+    }
+    const int n_sel = select ? k : total;
+    // winners above T go first (in entry order), then the earliest ties
+    int gpos = gt_before, epos = eq_before;
+#pragma unroll 1
+    for (int base = 0; base < my_count; base += kWave) {
+        const int i = base + l;
+        const bool in = i < my_count;
+        const uint32_t kv = in ? mk[i] : 0u;
+        const uint32_t ev = in ? me[i] : 0u;
+        const bool g = in && (!select || kv > T);
+        const bool e = in && select && kv == T;
+        const uint64_t bg = ballot(g), be = ballot(e);
+        if (g) {
+            const int p = gpos + rank_below(bg);
+            sel_key[p] = kv;
+            sel_ent[p] = ev;
+        }
+        if (e) {
+            const int r = epos + rank_below(be);
+            if (r < kk) {
+                sel_key[gt_total + r] = kv;
+                sel_ent[gt_total + r] = ev;
+            }
+        }
+        gpos += popc64(bg);
+        epos += popc64(be);
+    }
+    __syncthreads();
+    if (wv == 0)
+        sort_pairs_and_write(sel_key, sel_ent, n_sel, k, out);
 }
 
 } // namespace csa
