@@ -59,7 +59,9 @@ typedef enum csa_status {
  * computes bit-identical scores and selections). */
 typedef enum csa_plan {
     CSA_PLAN_AUTO = 0,
-    CSA_PLAN_ROW_TILES = 1, /* workgroups own blocks of query rows and walk K tiles    */
+    CSA_PLAN_ROW_TILES = 1, /* workgroups own blocks of query rows and walk K tiles;
+                               W <= 65536 (entries are held in 16 bits), AUTO takes
+                               SPLIT_ROWS beyond that                                */
     CSA_PLAN_SPLIT_ROWS = 2 /* long rows split over workgroups (decode), then a top-k pass */
 } csa_plan;
 

@@ -87,7 +87,11 @@ csa_status check_problem(const csa_index_problem *p, Checked &c)
     int64_t row_blocks = (int64_t)p->B * ((p->S + csa::kRowsPerBlock - 1) / csa::kRowsPerBlock);
     int plan = p->plan;
     if (plan == CSA_PLAN_AUTO)
-        plan = (row_blocks < kMinRowBlocks && p->W >= kMinSplitW) ? CSA_PLAN_SPLIT_ROWS : CSA_PLAN_ROW_TILES;
+        plan = ((row_blocks < kMinRowBlocks && p->W >= kMinSplitW) || p->W > csa::kRowTilesMaxW)
+                   ? CSA_PLAN_SPLIT_ROWS
+                   : CSA_PLAN_ROW_TILES;
+    if (plan == CSA_PLAN_ROW_TILES && p->W > csa::kRowTilesMaxW)
+        return fail(CSA_ERR_UNSUPPORTED, "the row-tile plan takes W <= %d (got %d)", csa::kRowTilesMaxW, p->W);
     c.plan = plan;
     // grid sizes must fit a 32-bit launch
     int64_t chunks = (p->W + csa::kSplitChunk - 1) / csa::kSplitChunk;
@@ -362,6 +366,7 @@ csa_status csa_index_select(const csa_index_problem *p, const void *q, const voi
     }
 
     const int mode = csa::kModeSelect | (scores ? csa::kModeScores : 0);
+    a.cap = csa::rows_topk_capacity(top_k);
     size_t lds = csa::rows_lds_bytes(p->D, mode, a.cap);
     if ((st = device_lds_limit(lds, "row-tile select")) != CSA_OK)
         return st;

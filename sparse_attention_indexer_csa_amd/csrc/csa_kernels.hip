@@ -54,8 +54,15 @@ __device__ __forceinline__ float tile_scores(const RowOperand<HB, KS> &row, bool
 // mode & kModeSelect: each wave streams its row's scores through a TopKRow
 //                     candidate buffer in LDS and writes the row's top-k.
 // ---------------------------------------------------------------------------
+// Up to 64 heads a row's operands leave room for two waves per
+// SIMD (at most 256 VGPRs), so one wave's MFMA work hides the other's
+// epilogue and top-k bookkeeping; wider rows run one wave per SIMD.
+template <int D, int HB>
+constexpr int rows_waves_per_eu() { return HB <= 2 ? 2 : 1; }
+
 template <int D, int HB, int MODE>
-__global__ __launch_bounds__(kRowWaves * kWave) void rows_kernel(const KernelArgs a)
+__global__ __launch_bounds__(kRowWaves * kWave) __attribute__((amdgpu_waves_per_eu(rows_waves_per_eu<D, HB>())))
+void rows_kernel(const KernelArgs a)
 {
     using G = TileGeom<D>;
     constexpr int KS = G::kKs;
@@ -106,12 +113,13 @@ __global__ __launch_bounds__(kRowWaves * kWave) void rows_kernel(const KernelArg
             t_lo = w2 == 0 ? first_tile[0] : min(t_lo, first_tile[w2]);
     }
 
-    TopKRow tk;
+    // per wave: 256-bin histogram, cap keys, cap 16-bit entries
+    TopKRow<uint16_t> tk;
     if (MODE & kModeSelect) {
-        unsigned char *base = smem + 2 * G::kTileBytes + (size_t)wv * (1024 + (size_t)a.cap * 8);
+        unsigned char *base = smem + 2 * G::kTileBytes + (size_t)wv * rows_topk_wave_bytes(a.cap);
         uint32_t *hist = reinterpret_cast<uint32_t *>(base);
         uint32_t *key = hist + 256;
-        topk_init(tk, key, key + a.cap, hist, a.cap, a.top_k);
+        topk_init(tk, key, reinterpret_cast<uint16_t *>(key + a.cap), hist, a.cap, a.top_k);
     }
 
     const uint16_t *kb = a.k + b * a.k_sb;
@@ -319,7 +327,7 @@ __device__ __forceinline__ int row_length(const KernelArgs &a, int64_t row)
 
 // Stream src[j0 .. j1) (j1 - j0 a multiple of 64 or the row end n) into the
 // wave's buffer, eight 64-entry chunks per batch of loads.
-__device__ __forceinline__ void stream_row(TopKRow &tk, const float *src, int j0, int j1, int n)
+__device__ __forceinline__ void stream_row(TopKRow<uint32_t> &tk, const float *src, int j0, int j1, int n)
 {
     const int l = lane();
     constexpr int kBatch = 8;
@@ -352,7 +360,7 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(const KernelAr
     unsigned char *base = smem + (size_t)wv * (1024 + (size_t)a.cap * 8);
     uint32_t *hist = reinterpret_cast<uint32_t *>(base);
     uint32_t *key = hist + 256;
-    TopKRow tk;
+    TopKRow<uint32_t> tk;
     topk_init(tk, key, key + a.cap, hist, a.cap, a.top_k);
     if (n > 0)
         stream_row(tk, a.scores + row * a.W, 0, n, n);
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(con
     const int chunks = (n + kWave - 1) / kWave;
     const int per = (chunks + kTopkBlockWaves - 1) / kTopkBlockWaves;
     const int j0 = min(wv * per * kWave, n), j1 = min((wv + 1) * per * kWave, n);
-    TopKRow tk;
+    TopKRow<uint32_t> tk;
     topk_init(tk, keys + (size_t)wv * a.cap, ents + (size_t)wv * a.cap, hist_all + wv * 256, a.cap, a.top_k);
     if (j1 > j0)
         stream_row(tk, a.scores + row * a.W, j0, j1, n);
@@ -395,7 +403,7 @@ __global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(con
 size_t rows_lds_bytes(int D, int mode, int cap)
 {
     size_t tile = 2 * (size_t)kTileEntries * (D + 8) * 2;
-    size_t sel = (mode & kModeSelect) ? (size_t)kRowWaves * (1024 + (size_t)cap * 8) : 0;
+    size_t sel = (mode & kModeSelect) ? (size_t)kRowWaves * rows_topk_wave_bytes(cap) : 0;
     return tile + sel;
 }
 

@@ -47,8 +47,15 @@ constexpr int kTopkBlockMinLen = 8192;
 enum { kModeScores = 1, kModeSelect = 2 };
 
 // Candidate-buffer capacity of the streaming top-k for a given k (room for at
-// least one more 64-pair push after a compaction down to k).
+// least one more 64-pair push after a compaction down to k).  The row-tile
+// kernel stores 16-bit entries and affords a larger buffer, so most rows never
+// compact mid-stream.
 __host__ __device__ constexpr int topk_capacity(int k) { return ((k + 63) / 64) * 64 + 512; }
+__host__ __device__ constexpr int rows_topk_capacity(int k) { return ((k + 63) / 64) * 64 + 1024; }
+// LDS bytes of one wave's row-tile buffer: histogram, keys, 16-bit entries.
+__host__ __device__ constexpr size_t rows_topk_wave_bytes(int cap) { return 1024 + (size_t)cap * 6; }
+// Entries of the row-tile plan are stored in 16 bits.
+constexpr int kRowTilesMaxW = 65536;
 
 size_t rows_lds_bytes(int D, int mode, int cap);
 size_t topk_lds_bytes(int cap);

@@ -25,9 +25,10 @@
 
 namespace csa {
 
+template <typename EntT>
 struct TopKRow {
     uint32_t *key;  // LDS [cap]
-    uint32_t *ent;  // LDS [cap]
+    EntT *ent;      // LDS [cap]
     uint32_t *hist; // LDS [256], scratch of the owning wave
     int cap;        // >= k + 64
     int k;
@@ -35,7 +36,8 @@ struct TopKRow {
     uint32_t tau;   // wave-uniform
 };
 
-__device__ __forceinline__ void topk_init(TopKRow &t, uint32_t *key, uint32_t *ent, uint32_t *hist, int cap, int k)
+template <typename EntT>
+__device__ __forceinline__ void topk_init(TopKRow<EntT> &t, uint32_t *key, EntT *ent, uint32_t *hist, int cap, int k)
 {
     t.key = key;
     t.ent = ent;
@@ -76,40 +78,77 @@ __device__ __forceinline__ int find_digit(const uint32_t *hist, int kk, int &abo
     return read_lane(found, src) & 0xFF;
 }
 
+// Smallest and largest key of key[0..count), count >= 1.
+__device__ __forceinline__ void key_range(const uint32_t *key, int count, uint32_t &lo, uint32_t &hi)
+{
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int i = lane(); i < count; i += kWave) {
+        const uint32_t kv = key[i];
+        mn = min(mn, kv);
+        mx = max(mx, kv);
+    }
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, d, kWave));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, kWave));
+    }
+    lo = uniform_u(mn);
+    hi = uniform_u(mx);
+}
+
+// Histogram of the keys in [base, base + span] by (key - base) >> shift
+// (at most 256 buckets), then the bucket holding the kk-th largest of them.
+__device__ __forceinline__ int bucket_of_kth(const uint32_t *key, int count, uint32_t base, uint32_t span, int shift,
+                                             int kk, uint32_t *hist, int &above)
+{
+    for (int b = lane(); b < 256; b += kWave)
+        hist[b] = 0u;
+    wave_lds_fence();
+    for (int i = lane(); i < count; i += kWave) {
+        const uint32_t off = key[i] - base;
+        if (off <= span)
+            atomicAdd(&hist[off >> shift], 1u);
+    }
+    wave_lds_fence();
+    const int d = find_digit(hist, kk, above);
+    wave_lds_fence();
+    return d;
+}
+
 // Radix select over key[0..count), count > k: the k-th largest key T, and how
 // many keys equal to T belong to the top k (the earliest ones in buffer order).
+// The digits adapt to the keys' actual range: each pass splits the current
+// range [base, base + span] into at most 256 buckets, so scores that share
+// their leading bits still spread over many buckets.
 __device__ __forceinline__ void radix_select(const uint32_t *key, int count, int k, uint32_t *hist, uint32_t &T,
                                              int &ties_keep)
 {
-    const int l = lane();
-    uint32_t prefix = 0u, mask = 0u;
-    int kk = k;
     wave_lds_fence();
+    uint32_t base, hi;
+    key_range(key, count, base, hi);
+    uint32_t span = hi - base;
+    int kk = k;
 #pragma unroll 1
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int bin = l; bin < 256; bin += kWave)
-            hist[bin] = 0u;
-        wave_lds_fence();
-        for (int i = l; i < count; i += kWave) {
-            const uint32_t kv = key[i];
-            if ((kv & mask) == prefix)
-                atomicAdd(&hist[(kv >> shift) & 0xFFu], 1u);
-        }
-        wave_lds_fence();
+    while (span != 0u) {
+        const int bits = 32 - __builtin_clz(span);
+        const int shift = bits > 8 ? bits - 8 : 0;
         int above;
-        const int digit = find_digit(hist, kk, above);
+        const uint32_t d = (uint32_t)bucket_of_kth(key, count, base, span, shift, kk, hist, above);
         kk -= above;
-        prefix |= (uint32_t)digit << shift;
-        mask |= 0xFFu << shift;
-        wave_lds_fence();
+        base += d << shift;
+        const uint32_t width = shift == 0 ? 0u : (1u << shift) - 1u;
+        span = min(span - (d << shift), width);
+        if (shift == 0)
+            break;
     }
-    T = prefix;
+    T = base;
     ties_keep = kk;
 }
 
 // Keep keys > T and the first ties_keep keys == T, in place and in order.
 // Returns the new count.
-__device__ __forceinline__ int compact_keep(uint32_t *key, uint32_t *ent, int count, uint32_t T, int ties_keep)
+template <typename EntT>
+__device__ __forceinline__ int compact_keep(uint32_t *key, EntT *ent, int count, uint32_t T, int ties_keep)
 {
     int out = 0, ties = 0;
 #pragma unroll 1
@@ -117,7 +156,7 @@ __device__ __forceinline__ int compact_keep(uint32_t *key, uint32_t *ent, int co
         const int i = base + lane();
         const bool in = i < count;
         const uint32_t kv = in ? key[i] : 0u;
-        const uint32_t ev = in ? ent[i] : 0u;
+        const EntT ev = in ? ent[i] : (EntT)0;
         const bool eq = in && kv == T;
         const uint64_t beq = ballot(eq);
         const bool keep = (in && kv > T) || (eq && ties + rank_below(beq) < ties_keep);
@@ -134,8 +173,9 @@ __device__ __forceinline__ int compact_keep(uint32_t *key, uint32_t *ent, int co
     return out;
 }
 
-// Reduce the buffer to its top k (no-op when it holds at most k pairs).
-__device__ __forceinline__ void topk_reduce(TopKRow &t)
+// Reduce the buffer to exactly its top k (no-op when it holds at most k pairs).
+template <typename EntT>
+__device__ __forceinline__ void topk_reduce(TopKRow<EntT> &t)
 {
     if (t.count > t.k) {
         uint32_t T;
@@ -146,15 +186,44 @@ __device__ __forceinline__ void topk_reduce(TopKRow &t)
     }
 }
 
+// Make room in a full buffer cheaply: one range-adaptive histogram finds the
+// bucket holding the k-th largest key; every key at or above that bucket's
+// lower bound L is kept (at least k of them) and tau becomes L - 1.  A later
+// pair with key < L is beaten by those k kept keys, so dropping it is exact.
+// Falls back to the exact reduction when that would free too little.
+template <typename EntT>
+__device__ __forceinline__ void topk_make_room(TopKRow<EntT> &t)
+{
+    wave_lds_fence();
+    uint32_t lo, hi;
+    key_range(t.key, t.count, lo, hi);
+    const uint32_t span = hi - lo;
+    if (span != 0u) {
+        const int bits = 32 - __builtin_clz(span);
+        const int shift = bits > 8 ? bits - 8 : 0;
+        int above;
+        const uint32_t d = (uint32_t)bucket_of_kth(t.key, t.count, lo, span, shift, t.k, t.hist, above);
+        const int kept = above + (int)t.hist[d];
+        if (d > 0u && kept + 2 * kWave <= t.cap) {
+            const uint32_t L = lo + (d << shift);
+            t.count = uniform(compact_keep(t.key, t.ent, t.count, L - 1u, 0));
+            t.tau = uniform_u(L - 1u);
+            return;
+        }
+    }
+    topk_reduce(t);
+}
+
 // Offer one pair per lane; lanes must hold increasing entries, and every pair
 // offered later must have a larger entry.
-__device__ __forceinline__ void topk_push(TopKRow &t, uint32_t kv, uint32_t entry, bool valid)
+template <typename EntT>
+__device__ __forceinline__ void topk_push(TopKRow<EntT> &t, uint32_t kv, uint32_t entry, bool valid)
 {
     bool pass = valid && kv > t.tau;
     uint64_t bal = ballot(pass);
     int n = popc64(bal);
     if (t.count + n > t.cap) {
-        topk_reduce(t);
+        topk_make_room(t);
         pass = valid && kv > t.tau;
         bal = ballot(pass);
         n = popc64(bal);
@@ -162,7 +231,7 @@ __device__ __forceinline__ void topk_push(TopKRow &t, uint32_t kv, uint32_t entr
     if (pass) {
         const int pos = t.count + rank_below(bal);
         t.key[pos] = kv;
-        t.ent[pos] = entry;
+        t.ent[pos] = (EntT)entry;
     }
     t.count += n;
 }
@@ -256,8 +325,8 @@ __device__ __forceinline__ void bitonic_sort_desc(uint64_t (&v)[E])
 }
 
 // Sort the n pairs key/ent[0..n) and write out[0..k): entries, then -1.
-template <int E>
-__device__ __forceinline__ void sort_and_write(const uint32_t *key, const uint32_t *ent, int n, int k, int32_t *out)
+template <int E, typename EntT>
+__device__ __forceinline__ void sort_and_write(const uint32_t *key, const EntT *ent, int n, int k, int32_t *out)
 {
     const int l = lane();
     uint64_t v[E];
@@ -265,7 +334,7 @@ __device__ __forceinline__ void sort_and_write(const uint32_t *key, const uint32
     for (int r = 0; r < E; ++r) {
         const int e = l * E + r;
         // ~entry in the low half: among equal keys the lower entry sorts first.
-        v[r] = (e < n) ? (((uint64_t)key[e] << 32) | (uint32_t)~ent[e]) : 0ull;
+        v[r] = (e < n) ? (((uint64_t)key[e] << 32) | (uint32_t)~(uint32_t)ent[e]) : 0ull;
     }
     bitonic_sort_desc<E>(v);
 #pragma unroll
@@ -278,26 +347,27 @@ __device__ __forceinline__ void sort_and_write(const uint32_t *key, const uint32
         out[e] = -1;
 }
 
-__device__ __forceinline__ void sort_pairs_and_write(const uint32_t *key, const uint32_t *ent, int n, int k,
-                                                     int32_t *out)
+template <typename EntT>
+__device__ __forceinline__ void sort_pairs_and_write(const uint32_t *key, const EntT *ent, int n, int k, int32_t *out)
 {
     wave_lds_fence();
     if (n <= 64)
-        sort_and_write<1>(key, ent, n, k, out);
+        sort_and_write<1, EntT>(key, ent, n, k, out);
     else if (n <= 128)
-        sort_and_write<2>(key, ent, n, k, out);
+        sort_and_write<2, EntT>(key, ent, n, k, out);
     else if (n <= 256)
-        sort_and_write<4>(key, ent, n, k, out);
+        sort_and_write<4, EntT>(key, ent, n, k, out);
     else if (n <= 512)
-        sort_and_write<8>(key, ent, n, k, out);
+        sort_and_write<8, EntT>(key, ent, n, k, out);
     else if (n <= 1024)
-        sort_and_write<16>(key, ent, n, k, out);
+        sort_and_write<16, EntT>(key, ent, n, k, out);
     else
-        sort_and_write<32>(key, ent, n, k, out);
+        sort_and_write<32, EntT>(key, ent, n, k, out);
 }
 
 // Final selection of the row into out[0..k) (global memory).
-__device__ __forceinline__ void topk_finish(TopKRow &t, int32_t *out)
+template <typename EntT>
+__device__ __forceinline__ void topk_finish(TopKRow<EntT> &t, int32_t *out)
 {
     topk_reduce(t);
     sort_pairs_and_write(t.key, t.ent, t.count, t.k, out);

@@ -108,6 +108,14 @@ def test_plans_and_workspace_sizes(lib):
     # short rows are not split even when there are few of them
     p = prob(B=1, S=256, H=4, D=32, W=64)
     assert lib.csa_index_resolve_plan(ctypes.byref(p)) == 1
+    # the row-tile plan holds entries in 16 bits: W <= 65536
+    p = prob(B=1, S=16384, H=64, D=128, W=65536)
+    assert lib.csa_index_resolve_plan(ctypes.byref(p)) == 1
+    p = prob(B=1, S=16384, H=64, D=128, W=65537)
+    assert lib.csa_index_resolve_plan(ctypes.byref(p)) == 2
+    p = prob(B=1, S=16384, H=64, D=128, W=65537, plan=1)
+    assert lib.csa_index_resolve_plan(ctypes.byref(p)) == -1
+    assert ws_size(lib, p, 512)[0] == UNSUPPORTED
 
 
 def masks(q_offset=None, q_seg=None, k_seg=None):

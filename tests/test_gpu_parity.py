@@ -228,6 +228,25 @@ def test_edge_shapes_exact(case, plan):
         assert_scores_close(to_np(gpu_score(P, plan=plan)).reshape(P.rows, W), s_o, exact=True, what=str(case))
 
 
+@pytest.mark.parametrize("W,plans", [(65536, ("row_tiles", "split_rows")), (65537, ("auto",))])
+def test_widest_row_tile_cache(W, plans):
+    """The row-tile plan keeps entry numbers in 16 bits: W = 65536 is its
+    widest cache (the last entry is 65535); one more entry goes to the split
+    plan, and forcing the row-tile plan there is refused."""
+    P = make_problem(1, 3, 16, 32, W, 1, 2048, dist="int", seed=W, q_offset=np.array([W + 5], np.int32))
+    # the last entry duplicates row 0's best one, so it is selected
+    best = int(oracle.select(P)[1][0, 0])
+    P.k[0, W - 1] = P.k[0, best]
+    s_o, i_o = oracle.select(P)
+    assert (i_o[0] == W - 1).any()
+    for plan in plans:
+        idx = gpu_select(P, plan=plan)
+        assert_topk_match(to_np(idx).reshape(P.rows, -1), i_o, s_o, exact=True, what=f"W={W} {plan}")
+    if W > 65536:
+        with pytest.raises(csa.CsaUnsupportedError):
+            gpu_select(P, plan="row_tiles")
+
+
 def test_empty_batch_and_rows():
     for B, S in ((0, 10), (2, 0)):
         P = make_problem(B, S, 4, 32, 8, 4, 3, dist="int", seed=1)
