@@ -15,6 +15,8 @@ Also reported on the same line:
   decode        B=64 one-row decode over a 32768-entry cache (valid length
                 U[4096,32768]): rows/s and HBM fraction of the algorithmic bytes
   cpu_baseline  the CPU oracle (scores + top-k) on a bounded sample of the rows
+  copy          (leg "copy", off by default) a plain 1 GiB device copy, the
+                calibration kernel for the FETCH_SIZE / WRITE_SIZE counters
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -22,6 +24,7 @@ Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +38,37 @@ sys.path.insert(0, ROOT)
 METRIC = "indexer score entries/sec (causal) + % bf16 MFMA peak; decode rows/sec + % HBM BW"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+CSRC = os.path.join(ROOT, "sparse_attention_indexer_csa_amd", "csrc")
+
+# HBM bytes per launch of the fused prefill kernel, from FETCH_SIZE and
+# WRITE_SIZE counter runs scaled by what the same counters read for a plain
+# copy of known size.  Valid only for the kernel sources they were taken on
+# (sha256 over csrc/); reported as null otherwise.
+MEASURED_TRAFFIC = {
+    "sources_sha": "c9ee57ed7b11b2697ca0e4cd7234307d2b22423e703f33b4f744800a8e165a3d",
+    # FETCH_SIZE 140300 KiB x 1.99998 (copy calibration) + WRITE_SIZE 32768 KiB x 1.0
+    "bytes_per_launch": 320_886_000,
+}
+
+
+def sources_sha():
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    t = MEASURED_TRAFFIC
+    if t is None or t["sources_sha"] != sources_sha():
+        return None
+    return t["bytes_per_launch"]
+
+
+def row_kernel_name(P):
+    hb = 1 if P.H <= 32 else 2 if P.H <= 64 else 4
+    return f"csa::rows_kernel<{P.D}, {hb}, 2>"
 
 
 def log(*a):
@@ -47,7 +81,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--legs", default="select,score,decode,cpu",
-                    help="comma list of: select, score, decode, cpu")
+                    help="comma list of: select, score, decode, cpu, copy")
     ap.add_argument("--cpu-row-stride", type=int, default=2,
                     help="the CPU baseline runs every n-th row of the prefill workload")
     return ap.parse_args()
@@ -146,9 +180,9 @@ def main():
         result["ms_per_step"] = wall
         achieved = flops / (ev * 1e-3) / 1e12
         result["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                              "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                              "kernel": "rows_kernel<128,4,select>", "kernel_ms": ev,
-                              "flops_per_launch": flops}
+                              "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                              "kernel": row_kernel_name(P), "kernel_ms": ev,
+                              "flops_per_launch": flops, "sources_sha": sources_sha()[:16]}
         log(f"select: {wall:.3f} ms/step, kernel {ev:.3f} ms, {achieved:.1f} TFLOP/s")
 
     if "score" in legs:
@@ -189,6 +223,19 @@ def main():
                             "hbm_frac": gbs / PEAK_HBM_GBS,
                             "plan": csa.resolve_plan(dd["q"], dd["k"], dd["w"], Pd.m)}
         del caches, dd, ws
+
+    if "copy" in legs:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+
+        def step_c(_):
+            dst.copy_(src)
+
+        log("copy leg")
+        wall, ev = time_calls(step_c, args.steps, args.warmup, torch)
+        result["copy"] = {"bytes_read": n, "bytes_written": n, "call_ms": ev, "GB_s": 2 * n / (ev * 1e-3) / 1e9}
+        del src, dst
 
     if "cpu" in legs:
         import oracle

@@ -72,7 +72,7 @@ void rows_kernel(const KernelArgs a)
     uint16_t *ktile = reinterpret_cast<uint16_t *>(smem);
 
     const int tid = threadIdx.x;
-    const int wv = tid / kWave;
+    const int wv = uniform(tid / kWave);
     const int l = lane();
 
     const int rb = a.n_row_blocks - 1 - (int)(blockIdx.x / a.B);
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(const Kernel
 {
     constexpr int KS = D / 16;
     constexpr int kWaveEntries = kSplitTiles * kTileEntries;
-    const int wv = threadIdx.x / kWave;
+    const int wv = uniform(threadIdx.x / kWave);
     const int l = lane();
     const int64_t row_id = blockIdx.x / a.n_chunks;
     const int chunk = (int)(blockIdx.x % a.n_chunks);
@@ -352,7 +352,7 @@ __device__ __forceinline__ void stream_row(TopKRow<uint32_t> &tk, const float *s
 __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(const KernelArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int wv = threadIdx.x / kWave;
+    const int wv = uniform(threadIdx.x / kWave);
     const int64_t row = (int64_t)blockIdx.x * kTopkWaves + wv;
     if (row >= a.rows)
         return;
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(const KernelAr
 __global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(const KernelArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int wv = threadIdx.x / kWave;
+    const int wv = uniform(threadIdx.x / kWave);
     const int64_t row = blockIdx.x;
     const int n = row_length(a, row);
     uint32_t *hist_all = reinterpret_cast<uint32_t *>(smem);            // [kTopkBlockWaves][256]
