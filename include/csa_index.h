@@ -74,7 +74,8 @@ typedef enum csa_plan {
  *   k : [B,W,D] bf16 at k + b*k_sb + j*k_sw + t   (decode: W = cache capacity)
  *   w : [B,S,H] bf16 at w + b*w_sb + i*w_ss + h
  * Supported: D in {32, 64, 128}; 1 <= H <= 128; q and k 16-byte aligned with
- * strides that are multiples of 8 elements; W <= 2^30; m >= 1; finite scale.
+ * strides that are multiples of 8 elements; k_sw < 2^24; W <= 2^30; m >= 1;
+ * finite scale.
  */
 typedef struct csa_index_problem {
     int32_t B, S, H, D, W;

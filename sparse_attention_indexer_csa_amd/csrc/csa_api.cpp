@@ -35,6 +35,7 @@ csa_status ok()
 constexpr int kMaxTopK = 2048;
 constexpr int kMaxW = 1 << 30;
 constexpr int kNumCUs = 256; // MI355X; only used to choose a plan
+constexpr int64_t kMaxKeyStride = int64_t(1) << 24;
 // A row-tile launch with fewer workgroups than this leaves the chip idle.
 constexpr int64_t kMinRowBlocks = 2 * kNumCUs;
 // Rows shorter than this are not worth splitting.
@@ -82,6 +83,9 @@ csa_status check_problem(const csa_index_problem *p, Checked &c)
         return fail(CSA_ERR_INVALID_ARG, "strides must be non-negative");
     if ((p->q_sb | p->q_sh | p->q_ss | p->k_sb | p->k_sw) % 8 != 0)
         return fail(CSA_ERR_UNSUPPORTED, "q and k strides must be multiples of 8 elements (16-byte rows)");
+    if (p->k_sw >= kMaxKeyStride)
+        return fail(CSA_ERR_UNSUPPORTED, "k_sw=%lld not below %lld (key tiles are addressed with 32-bit offsets)",
+                    (long long)p->k_sw, (long long)kMaxKeyStride);
     c.rows = (int64_t)p->B * p->S;
     c.HB = head_blocks(p->H);
     int64_t row_blocks = (int64_t)p->B * ((p->S + csa::kRowsPerBlock - 1) / csa::kRowsPerBlock);

@@ -9,15 +9,38 @@
 
 namespace csa {
 
+// LDS image of a key tile: kTileEntries rows of D bf16 with a 16-byte pad
+// per row (row pitch D+8 elements), so the 16-byte B-fragment reads of
+// consecutive entries fall in different bank groups.  The tile is filled by
+// buffer-to-LDS DMA: instruction x writes the 64 consecutive 16-byte slots
+// 64x .. 64x+63 of the image, lane l the slot 64x+l; slot s holds chunk
+// s % kRowChunks of entry s / kRowChunks (pad slots receive whatever follows
+// the entry and are never read).  A tile is kRowChunks instructions.
 template <int D>
 struct TileGeom {
     static constexpr int kKs = D / 16;                      // MFMA k-steps per entry
     static constexpr int kPitch = D + 8;                    // LDS row pitch (elements): +16 B
-    static constexpr int kChunks = kTileEntries * D / 8;    // 16-byte pieces per tile
-    static constexpr int kPerThread = kChunks / (kRowWaves * kWave);
+    static constexpr int kRowChunks = kPitch / 8;           // 16-byte slots per LDS row
+    static constexpr int kDmaOps = kRowChunks;              // 64 * kRowChunks slots / 64 lanes
+    static constexpr int kDmaPerWave = (kDmaOps + kRowWaves - 1) / kRowWaves;
     static constexpr int kTileElems = kTileEntries * kPitch;
     static constexpr size_t kTileBytes = (size_t)kTileElems * 2;
 };
+
+// Buffer resource over `bytes` bytes at `base` (raw, 32-bit elements): loads
+// at or beyond `bytes` return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
+}
+
+// Waits for this wave's outstanding vector-memory operations (the tile DMA).
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Scores of the 64 entries j0 .. j0+63 of one row: lane l returns the
 // scaled score of entry j0 + l.  Subtiles (32 entries) flagged off are not
@@ -122,26 +145,26 @@ void rows_kernel(const KernelArgs a)
         topk_init(tk, key, reinterpret_cast<uint16_t *>(key + a.cap), hist, a.cap, a.top_k);
     }
 
+    // Key tiles arrive by DMA (no registers, no address arithmetic per tile):
+    // the buffer resource covers the tile's entries that exist, so slots of
+    // entries at or past W read zeros (those entries are always masked).
     const uint16_t *kb = a.k + b * a.k_sb;
-    u32x4 pre[G::kPerThread];
+    uint32_t dma_off[G::kDmaPerWave];
+#pragma unroll
+    for (int x = 0; x < G::kDmaPerWave; ++x) {
+        const int slot = (wv + x * kRowWaves) * kWave + l;
+        dma_off[x] = (uint32_t)((slot / G::kRowChunks) * a.k_sw * 2 + (slot % G::kRowChunks) * 16);
+    }
     auto fetch = [&](int t) {
+        const int64_t e0 = (int64_t)t * kTileEntries;
+        const int n = min(a.W - (int)e0, kTileEntries);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(kb + e0 * a.k_sw, n * (int)a.k_sw * 2);
+        unsigned char *dst = smem + (size_t)(t & 1) * G::kTileBytes;
 #pragma unroll
-        for (int x = 0; x < G::kPerThread; ++x) {
-            const int c = tid + x * kRowWaves * kWave;
-            const int e = c / (D / 8), p = c % (D / 8);
-            // Entries past W are always masked: read a clamped in-bounds row
-            // instead of zero-filling, so no wait is needed before compute.
-            const int j = min(t * kTileEntries + e, a.W - 1);
-            pre[x] = *reinterpret_cast<const u32x4 *>(kb + (int64_t)j * a.k_sw + p * 8);
-        }
-    };
-    auto stash = [&](int buf) {
-        uint16_t *dst = ktile + buf * G::kTileElems;
-#pragma unroll
-        for (int x = 0; x < G::kPerThread; ++x) {
-            const int c = tid + x * kRowWaves * kWave;
-            const int e = c / (D / 8), p = c % (D / 8);
-            *reinterpret_cast<u32x4 *>(dst + e * G::kPitch + p * 8) = pre[x];
+        for (int x = 0; x < G::kDmaPerWave; ++x) {
+            const int op = wv + x * kRowWaves;
+            if (op < G::kDmaOps)
+                dma16(r, dst + op * kWave * 16, dma_off[x]);
         }
     };
     auto emit = [&](int tt, float s, bool valid) {
@@ -162,16 +185,16 @@ void rows_kernel(const KernelArgs a)
         return v;
     };
 
-    // The first key tile's loads go out before the row operands' so the two
-    // latencies overlap.
+    // The first key tile's DMA goes out before the row operands' loads so the
+    // two latencies overlap.  Each iteration then waits for its own DMA,
+    // meets the other waves at the barrier (tile t complete, tile t-1's buffer
+    // free) and starts the DMA of tile t+1 into that buffer.
     if (ntiles > t_lo)
         fetch(t_lo);
     RowOperand<HB, KS> row;
     if (active)
         load_row<HB, KS>(row, a.q + b * a.q_sb + (int64_t)i * a.q_ss, a.q_sh, a.w + b * a.w_sb + (int64_t)i * a.w_ss,
                          a.H);
-    if (ntiles > t_lo)
-        stash(t_lo & 1);
     if (PIPE) {
         // Software pipeline over tiles: the MFMAs of subtile 0 of tile t run
         // alongside the epilogue of subtile 1 of tile t-1, and the MFMAs of
@@ -185,9 +208,10 @@ void rows_kernel(const KernelArgs a)
         float p0 = 0.0f;
         bool prev_valid = false;
         for (int t = t_lo; t < ntiles; ++t) {
+            wait_vm();
+            __syncthreads();
             if (t + 1 < ntiles)
                 fetch(t + 1);
-            __syncthreads();
             if (active) {
                 const uint16_t *tile = ktile + (t & 1) * G::kTileElems;
                 const bool valid = tile_valid(t);
@@ -210,16 +234,15 @@ void rows_kernel(const KernelArgs a)
                 }
                 prev_valid = valid;
             }
-            if (t + 1 < ntiles)
-                stash((t + 1) & 1);
         }
         if (active && ntiles > t_lo)
             emit(ntiles - 1, scaled_score(combine_halves(p0, logits_partial<HB, KS>(row, c1)), a.scale), prev_valid);
     } else {
         for (int t = t_lo; t < ntiles; ++t) {
+            wait_vm();
+            __syncthreads();
             if (t + 1 < ntiles)
                 fetch(t + 1);
-            __syncthreads();
             if (active) {
                 const uint16_t *tile = ktile + (t & 1) * G::kTileElems;
                 const bool valid = tile_valid(t);
@@ -228,8 +251,6 @@ void rows_kernel(const KernelArgs a)
                 });
                 emit(t, s, valid);
             }
-            if (t + 1 < ntiles)
-                stash((t + 1) & 1);
         }
     }
     if (active && (MODE & kModeScores)) {
