@@ -72,17 +72,21 @@ __device__ __forceinline__ uint32_t uniform_u(uint32_t v) { return (uint32_t)__b
 __device__ __forceinline__ int read_lane(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 
 // Exclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_exclusive_sum(int v)
+// Inclusive prefix sum over the 64 lanes with DPP: shifts of 1, 2, 4, 8
+// inside each 16-lane row, then the last lane of row r is added to the rows
+// above it (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).
+__device__ __forceinline__ int wave_inclusive_sum(int x)
 {
-    int x = v;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int y = __shfl_up(x, d, kWave);
-        if (lane() >= d)
-            x += y;
-    }
-    return x - v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false); // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false); // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false); // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false); // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false); // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false); // row_bcast:31
+    return x;
 }
+
+__device__ __forceinline__ int wave_exclusive_sum(int v) { return wave_inclusive_sum(v) - v; }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask)
 {

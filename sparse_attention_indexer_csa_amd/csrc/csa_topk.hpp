@@ -78,6 +78,33 @@ __device__ __forceinline__ int find_digit(const uint32_t *hist, int kk, int &abo
     return read_lane(found, src) & 0xFF;
 }
 
+// Value of v in lane (lane ^ LX), with VALU lane exchanges only: DPP quad
+// permutations for distances 1 and 2, a half-row mirror followed by a quad
+// reversal for 4, a row rotation for 8, and the gfx950 lane-swap
+// instructions for 16 and 32 (v passed as both operands; each lane keeps the
+// half that came from the other row / half).
+template <int LX>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v)
+{
+    if constexpr (LX == 1)
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false); // quad_perm [1,0,3,2]
+    else if constexpr (LX == 2)
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false); // quad_perm [2,3,0,1]
+    else if constexpr (LX == 4) {
+        const int m = __builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false); // row_half_mirror
+        return (uint32_t)__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false);    // quad_perm [3,2,1,0]
+    } else if constexpr (LX == 8)
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false); // row_ror:8
+    else if constexpr (LX == 16) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return ((lane() >> 4) & 1) ? sw[0] : sw[1];
+    } else {
+        static_assert(LX == 32, "lane distance must be a power of two below 64");
+        const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane() < 32) ? sw[1] : sw[0];
+    }
+}
+
 // Smallest and largest key of key[0..count), count >= 1.
 __device__ __forceinline__ void key_range(const uint32_t *key, int count, uint32_t &lo, uint32_t &hi)
 {
@@ -87,11 +114,18 @@ __device__ __forceinline__ void key_range(const uint32_t *key, int count, uint32
         mn = min(mn, kv);
         mx = max(mx, kv);
     }
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, d, kWave));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, d, kWave));
-    }
+    mn = min(mn, lane_xor_u32<1>(mn));
+    mx = max(mx, lane_xor_u32<1>(mx));
+    mn = min(mn, lane_xor_u32<2>(mn));
+    mx = max(mx, lane_xor_u32<2>(mx));
+    mn = min(mn, lane_xor_u32<4>(mn));
+    mx = max(mx, lane_xor_u32<4>(mx));
+    mn = min(mn, lane_xor_u32<8>(mn));
+    mx = max(mx, lane_xor_u32<8>(mx));
+    mn = min(mn, lane_xor_u32<16>(mn));
+    mx = max(mx, lane_xor_u32<16>(mx));
+    mn = min(mn, lane_xor_u32<32>(mn));
+    mx = max(mx, lane_xor_u32<32>(mx));
     lo = uniform_u(mn);
     hi = uniform_u(mx);
 }
@@ -115,11 +149,59 @@ __device__ __forceinline__ int bucket_of_kth(const uint32_t *key, int count, uin
     return d;
 }
 
+// Bitonic sort of one u32 per lane (64 values) into descending lane order.
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint32_t bitonic_u32_level(uint32_t v, int l)
+{
+    const uint32_t o = lane_xor_u32<STRIDE>(v);
+    const bool keep_max = ((l & STRIDE) == 0) == ((l & SIZE) == 0);
+    v = keep_max ? max(v, o) : min(v, o);
+    if constexpr (STRIDE > 1)
+        return bitonic_u32_level<SIZE, STRIDE / 2>(v, l);
+    else
+        return v;
+}
+
+template <int SIZE = 2>
+__device__ __forceinline__ uint32_t sort_u32_desc(uint32_t v, int l)
+{
+    v = bitonic_u32_level<SIZE, SIZE / 2>(v, l);
+    if constexpr (SIZE < kWave)
+        return sort_u32_desc<SIZE * 2>(v, l);
+    else
+        return v;
+}
+
+// The n (<= 64) keys of key[0..count) that lie in [base, base + span], one
+// per lane (lane order = buffer order; lanes >= n get 0, below every
+// selectable key).  `scratch` holds at least 64 words.
+__device__ __forceinline__ uint32_t gather_range(const uint32_t *key, int count, uint32_t base, uint32_t span, int n,
+                                                 uint32_t *scratch)
+{
+    int out = 0;
+#pragma unroll 1
+    for (int b0 = 0; b0 < count && out < n; b0 += kWave) {
+        const int i = b0 + lane();
+        const uint32_t kv = i < count ? key[i] : 0u;
+        const bool in = i < count && kv - base <= span;
+        const uint64_t bal = ballot(in);
+        if (in)
+            scratch[out + rank_below(bal)] = kv;
+        out += popc64(bal);
+    }
+    wave_lds_fence();
+    const uint32_t x = lane() < n ? scratch[lane()] : 0u;
+    wave_lds_fence();
+    return x;
+}
+
 // Radix select over key[0..count), count > k: the k-th largest key T, and how
 // many keys equal to T belong to the top k (the earliest ones in buffer order).
 // The digits adapt to the keys' actual range: each pass splits the current
 // range [base, base + span] into at most 256 buckets, so scores that share
-// their leading bits still spread over many buckets.
+// their leading bits still spread over many buckets.  Once the bucket that
+// holds the k-th key has at most 64 keys, they are gathered into one
+// register per lane and sorted there instead of running more passes.
 __device__ __forceinline__ void radix_select(const uint32_t *key, int count, int k, uint32_t *hist, uint32_t &T,
                                              int &ties_keep)
 {
@@ -134,12 +216,19 @@ __device__ __forceinline__ void radix_select(const uint32_t *key, int count, int
         const int shift = bits > 8 ? bits - 8 : 0;
         int above;
         const uint32_t d = (uint32_t)bucket_of_kth(key, count, base, span, shift, kk, hist, above);
+        const int inb = uniform((int)hist[d]);
         kk -= above;
         base += d << shift;
-        const uint32_t width = shift == 0 ? 0u : (1u << shift) - 1u;
-        span = min(span - (d << shift), width);
         if (shift == 0)
             break;
+        span = min(span - (d << shift), (1u << shift) - 1u);
+        if (inb <= kWave) {
+            wave_lds_fence();
+            const uint32_t sx = sort_u32_desc(gather_range(key, count, base, span, inb, hist), lane());
+            T = uniform_u(read_lane((int)sx, kk - 1));
+            ties_keep = kk - popc64(ballot(sx > T));
+            return;
+        }
     }
     T = base;
     ties_keep = kk;
@@ -238,30 +327,10 @@ __device__ __forceinline__ void topk_push(TopKRow<EntT> &t, uint32_t kv, uint32_
 
 // ---------------------------------------------------------------------------
 // Bitonic sort of 64*E values held by one wave, lane l holding elements
-// l*E .. l*E+E-1, into descending order.  Partners at lane distance 1, 2 and
-// 8 are fetched with DPP, 4 and 16 with a swizzle, 32 with the gfx950 lane
-// swap; partners inside a lane are plain registers.
+// l*E .. l*E+E-1, into descending order.  Partners in other lanes come from
+// lane_xor_u32 (VALU exchanges only); partners inside a lane are plain
+// registers.
 // ---------------------------------------------------------------------------
-template <int LX>
-__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v)
-{
-    if constexpr (LX == 1)
-        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false); // quad_perm [1,0,3,2]
-    else if constexpr (LX == 2)
-        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false); // quad_perm [2,3,0,1]
-    else if constexpr (LX == 8)
-        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false); // row_ror:8
-    else if constexpr (LX == 4)
-        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F); // xor 4 within 32 lanes
-    else if constexpr (LX == 16)
-        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F); // xor 16 within 32 lanes
-    else {
-        // lane distance 32: swap the halves (v itself gives the other half)
-        const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-        return (lane() < 32) ? sw[1] : sw[0];
-    }
-}
-
 // One cross-lane stage: partners at lane distance LX.  For these stages the
 // keep-larger flag depends only on the lane (stride and size are multiples
 // of E), so it is computed once.
@@ -301,26 +370,52 @@ __device__ __forceinline__ void bitonic_in_lane(uint64_t (&v)[E], int size, int 
     }
 }
 
+// Fully unrolled network (E <= 8): every stage's lane exchange and
+// direction are compile-time, so a stage is exchanges + compare + selects.
+template <int E, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_cross_levels(uint64_t (&v)[E], int l)
+{
+    if constexpr (STRIDE >= E && STRIDE >= 1) {
+        const int e = l * E;
+        const bool keep_max = ((e & STRIDE) == 0) == ((e & SIZE) == 0);
+        cross_stage<STRIDE / E, E>(v, keep_max);
+        bitonic_cross_levels<E, SIZE, STRIDE / 2>(v, l);
+    }
+}
+
+template <int E, int SIZE>
+__device__ __forceinline__ void bitonic_levels(uint64_t (&v)[E], int l)
+{
+    bitonic_cross_levels<E, SIZE, SIZE / 2>(v, l);
+    bitonic_in_lane<E>(v, SIZE, l);
+    if constexpr (SIZE < kWave * E)
+        bitonic_levels<E, SIZE * 2>(v, l);
+}
+
 template <int E>
 __device__ __forceinline__ void bitonic_sort_desc(uint64_t (&v)[E])
 {
     const int l = lane();
+    if constexpr (E <= 8) {
+        bitonic_levels<E, 2>(v, l);
+    } else {
 #pragma unroll 1
-    for (int size = 2; size <= kWave * E; size <<= 1) {
+        for (int size = 2; size <= kWave * E; size <<= 1) {
 #pragma unroll 1
-        for (int stride = size >> 1; stride >= E; stride >>= 1) {
-            const int e = l * E;
-            const bool keep_max = ((e & stride) == 0) == ((e & size) == 0);
-            switch (stride / E) {
-            case 1: cross_stage<1, E>(v, keep_max); break;
-            case 2: cross_stage<2, E>(v, keep_max); break;
-            case 4: cross_stage<4, E>(v, keep_max); break;
-            case 8: cross_stage<8, E>(v, keep_max); break;
-            case 16: cross_stage<16, E>(v, keep_max); break;
-            default: cross_stage<32, E>(v, keep_max); break;
+            for (int stride = size >> 1; stride >= E; stride >>= 1) {
+                const int e = l * E;
+                const bool keep_max = ((e & stride) == 0) == ((e & size) == 0);
+                switch (stride / E) {
+                case 1: cross_stage<1, E>(v, keep_max); break;
+                case 2: cross_stage<2, E>(v, keep_max); break;
+                case 4: cross_stage<4, E>(v, keep_max); break;
+                case 8: cross_stage<8, E>(v, keep_max); break;
+                case 16: cross_stage<16, E>(v, keep_max); break;
+                default: cross_stage<32, E>(v, keep_max); break;
+                }
             }
+            bitonic_in_lane<E>(v, size, l);
         }
-        bitonic_in_lane<E>(v, size, l);
     }
 }
 
