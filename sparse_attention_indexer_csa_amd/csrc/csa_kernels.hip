@@ -149,23 +149,29 @@ void rows_kernel(const KernelArgs a)
     // the buffer resource covers the tile's entries that exist, so slots of
     // entries at or past W read zeros (those entries are always masked).
     const uint16_t *kb = a.k + b * a.k_sb;
+    const int entry_bytes = (int)a.k_sw * 2;
+    const int64_t tile_stride = (int64_t)kTileEntries * a.k_sw;
+    const int W = a.W;
     uint32_t dma_off[G::kDmaPerWave];
 #pragma unroll
     for (int x = 0; x < G::kDmaPerWave; ++x) {
         const int slot = (wv + x * kRowWaves) * kWave + l;
-        dma_off[x] = (uint32_t)((slot / G::kRowChunks) * a.k_sw * 2 + (slot % G::kRowChunks) * 16);
+        dma_off[x] = (uint32_t)((slot / G::kRowChunks) * entry_bytes + (slot % G::kRowChunks) * 16);
     }
+    // ops wv, wv+4, ...: all waves have the first kDmaOps / 4, the first
+    // kDmaOps % 4 waves one more
+    constexpr int kFullOps = G::kDmaOps / kRowWaves;
+    const bool extra_op = wv < G::kDmaOps % kRowWaves;
     auto fetch = [&](int t) {
-        const int64_t e0 = (int64_t)t * kTileEntries;
-        const int n = min(a.W - (int)e0, kTileEntries);
-        const __amdgpu_buffer_rsrc_t r = raw_rsrc(kb + e0 * a.k_sw, n * (int)a.k_sw * 2);
-        unsigned char *dst = smem + (size_t)(t & 1) * G::kTileBytes;
+        const int e0 = t * kTileEntries;
+        const int n = min(W - e0, kTileEntries);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(kb + t * tile_stride, n * entry_bytes);
+        unsigned char *dst = smem + (size_t)(t & 1) * G::kTileBytes + wv * kWave * 16;
 #pragma unroll
-        for (int x = 0; x < G::kDmaPerWave; ++x) {
-            const int op = wv + x * kRowWaves;
-            if (op < G::kDmaOps)
-                dma16(r, dst + op * kWave * 16, dma_off[x]);
-        }
+        for (int x = 0; x < kFullOps; ++x)
+            dma16(r, dst + x * kRowWaves * kWave * 16, dma_off[x]);
+        if (kFullOps < G::kDmaPerWave && extra_op)
+            dma16(r, dst + kFullOps * kRowWaves * kWave * 16, dma_off[G::kDmaPerWave - 1]);
     };
     auto emit = [&](int tt, float s, bool valid) {
         const int j = tt * kTileEntries + l;
@@ -265,8 +271,13 @@ void rows_kernel(const KernelArgs a)
         for (int j = max(ntiles, t_lo) * kTileEntries + l; j < a.W; j += kWave)
             a.scores[row_id * a.W + j] = -INFINITY;
     }
-    if (MODE & kModeSelect)
-        topk_finish(tk, a.idx + row_id * a.top_k);
+    if (MODE & kModeSelect) {
+        // buffers of up to 1536 pairs (k <= 512) finish from registers
+        if (a.cap <= 24 * kWave)
+            topk_finish_regs<24>(tk, a.idx + row_id * a.top_k);
+        else
+            topk_finish(tk, a.idx + row_id * a.top_k);
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -343,10 +343,11 @@ __device__ __forceinline__ void cross_stage(uint64_t (&v)[E], bool keep_max)
         ohi[r] = lane_xor_u32<LX>((uint32_t)(v[r] >> 32));
         olo[r] = lane_xor_u32<LX>((uint32_t)v[r]);
     }
+    // distinct composites: keep v when (v > o) matches keep_max
 #pragma unroll
     for (int r = 0; r < E; ++r) {
         const uint64_t o = ((uint64_t)ohi[r] << 32) | olo[r];
-        v[r] = ((v[r] > o) == keep_max) ? v[r] : o;
+        v[r] = ((v[r] < o) != keep_max) ? v[r] : o;
     }
 }
 
@@ -370,6 +371,33 @@ __device__ __forceinline__ void bitonic_in_lane(uint64_t (&v)[E], int size, int 
     }
 }
 
+// In-lane stages of one level with the block size known at compile time.
+// Element r of lane l sorts descending iff bit SIZE of l*E + r is clear:
+// for SIZE < E that is a constant of r, otherwise it depends on the lane
+// only.  The composites are distinct, so "a > b" is "not a < b".
+template <int E, int SIZE>
+__device__ __forceinline__ void bitonic_in_lane_fixed(uint64_t (&v)[E], int l)
+{
+    const bool asc_lane = ((l * E) & SIZE) != 0;
+#pragma unroll
+    for (int stride = (SIZE / 2 < E / 2 ? SIZE / 2 : E / 2); stride >= 1; stride >>= 1) {
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+            if ((r & stride) == 0) {
+                const uint64_t a = v[r], b = v[r + stride];
+                const bool lt = a < b;
+                bool sw;
+                if constexpr (SIZE >= E)
+                    sw = lt != asc_lane;
+                else
+                    sw = ((r & SIZE) == 0) ? lt : !lt;
+                v[r] = sw ? b : a;
+                v[r + stride] = sw ? a : b;
+            }
+        }
+    }
+}
+
 // Fully unrolled network (E <= 8): every stage's lane exchange and
 // direction are compile-time, so a stage is exchanges + compare + selects.
 template <int E, int SIZE, int STRIDE>
@@ -387,7 +415,7 @@ template <int E, int SIZE>
 __device__ __forceinline__ void bitonic_levels(uint64_t (&v)[E], int l)
 {
     bitonic_cross_levels<E, SIZE, SIZE / 2>(v, l);
-    bitonic_in_lane<E>(v, SIZE, l);
+    bitonic_in_lane_fixed<E, SIZE>(v, l);
     if constexpr (SIZE < kWave * E)
         bitonic_levels<E, SIZE * 2>(v, l);
 }
@@ -466,6 +494,158 @@ __device__ __forceinline__ void topk_finish(TopKRow<EntT> &t, int32_t *out)
 {
     topk_reduce(t);
     sort_pairs_and_write(t.key, t.ent, t.count, t.k, out);
+}
+
+// Histogram of the register-held keys kr[] (0 = no key; every buffered key
+// is above the key of -inf, so never 0) that lie in [base, base + span], by
+// (key - base) >> shift, then the bucket holding the kk-th largest of them
+// (find_digit).  `inb` receives that bucket's count.
+template <int NR>
+__device__ __forceinline__ int bucket_of_kth_regs(const uint32_t (&kr)[NR], uint32_t base, uint32_t span, int shift,
+                                                  int kk, uint32_t *hist, int &above, int &inb)
+{
+    for (int b = lane(); b < 256; b += kWave)
+        hist[b] = 0u;
+    wave_lds_fence();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const uint32_t off = kr[r] - base;
+        if (kr[r] != 0u && off <= span)
+            atomicAdd(&hist[off >> shift], 1u);
+    }
+    wave_lds_fence();
+    const int d = find_digit(hist, kk, above);
+    inb = uniform((int)hist[d]);
+    wave_lds_fence();
+    return d;
+}
+
+// Final selection for buffers of at most 64*NR pairs, with the keys held in
+// registers: lane l holds the pairs at 256*m + 4*l + c (m < NR/4, c < 4).
+// One LDS read of every key and entry, range-adaptive histogram passes from
+// registers until the k-th key's bucket holds at most 64 keys, that bucket
+// sorted in registers, then the k winners (keys above T, and the earliest
+// ties) written back to the front of the buffer for the final sort.
+template <int NR, typename EntT>
+__device__ __forceinline__ void topk_finish_regs(TopKRow<EntT> &t, int32_t *out)
+{
+    static_assert(NR % 4 == 0, "four pairs per lane per group");
+    const int n = t.count, k = t.k, l = lane();
+    wave_lds_fence();
+    if (n <= k) {
+        sort_pairs_and_write(t.key, t.ent, n, k, out);
+        return;
+    }
+    uint32_t kr[NR];
+    EntT er[NR];
+#pragma unroll
+    for (int m = 0; m < NR / 4; ++m) {
+        // i0 < n <= cap, all multiples of 4: the group lies in the buffer
+        const int i0 = 256 * m + 4 * l;
+        const bool in = i0 < n;
+        const u32x4 q = in ? *reinterpret_cast<const u32x4 *>(t.key + i0) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            kr[4 * m + c] = i0 + c < n ? q[c] : 0u;
+            er[4 * m + c] = in ? t.ent[i0 + c] : (EntT)0;
+        }
+    }
+    // key range of the valid keys
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        mn = min(mn, kr[r] != 0u ? kr[r] : 0xFFFFFFFFu);
+        mx = max(mx, kr[r]);
+    }
+    mn = min(mn, lane_xor_u32<1>(mn));
+    mx = max(mx, lane_xor_u32<1>(mx));
+    mn = min(mn, lane_xor_u32<2>(mn));
+    mx = max(mx, lane_xor_u32<2>(mx));
+    mn = min(mn, lane_xor_u32<4>(mn));
+    mx = max(mx, lane_xor_u32<4>(mx));
+    mn = min(mn, lane_xor_u32<8>(mn));
+    mx = max(mx, lane_xor_u32<8>(mx));
+    mn = min(mn, lane_xor_u32<16>(mn));
+    mx = max(mx, lane_xor_u32<16>(mx));
+    mn = min(mn, lane_xor_u32<32>(mn));
+    mx = max(mx, lane_xor_u32<32>(mx));
+    uint32_t base = uniform_u(mn), span = uniform_u(mx) - base;
+    int kk = k;
+    uint32_t T = base;
+    int ties_keep = 0;
+    bool resolved = false;
+#pragma unroll 1
+    while (span != 0u) {
+        const int bits = 32 - __builtin_clz(span);
+        const int shift = bits > 8 ? bits - 8 : 0;
+        int above, inb;
+        const uint32_t d = (uint32_t)bucket_of_kth_regs<NR>(kr, base, span, shift, kk, t.hist, above, inb);
+        kk -= above;
+        base += d << shift;
+        if (shift == 0)
+            break;
+        span = min(span - (d << shift), (1u << shift) - 1u);
+        if (inb <= kWave) {
+            // gather the bucket's keys (any order), one per lane, and sort them
+            int cnt = 0;
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                cnt += (kr[r] != 0u && kr[r] - base <= span) ? 1 : 0;
+            int pos = wave_exclusive_sum(cnt);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                if (kr[r] != 0u && kr[r] - base <= span)
+                    t.hist[pos++] = kr[r];
+            }
+            wave_lds_fence();
+            const uint32_t x = l < inb ? t.hist[l] : 0u;
+            const uint32_t sx = sort_u32_desc(x, l);
+            T = uniform_u((uint32_t)read_lane((int)sx, kk - 1));
+            ties_keep = kk - popc64(ballot(sx > T));
+            resolved = true;
+            wave_lds_fence();
+            break;
+        }
+    }
+    if (!resolved) {
+        T = base;
+        ties_keep = kk;
+    }
+    // winners: keys > T at [0, k - ties_keep), the earliest ties after them
+    // (T is a buffered key, so no empty slot (0) compares equal to it)
+    const int n_gt = k - ties_keep;
+    int g_base = 0, e_base = 0;
+#pragma unroll
+    for (int m = 0; m < NR / 4; ++m) {
+        int gc = 0, ec = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            gc += kr[4 * m + c] > T ? 1 : 0;
+            ec += kr[4 * m + c] == T ? 1 : 0;
+        }
+        const int gi = wave_inclusive_sum(gc), ei = wave_inclusive_sum(ec);
+        int gp = g_base + gi - gc, ep = e_base + ei - ec;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int r = 4 * m + c;
+            if (kr[r] > T) {
+                t.key[gp] = kr[r];
+                t.ent[gp] = er[r];
+                ++gp;
+            } else if (kr[r] == T) {
+                if (ep < ties_keep) {
+                    t.key[n_gt + ep] = kr[r];
+                    t.ent[n_gt + ep] = er[r];
+                }
+                ++ep;
+            }
+        }
+        g_base += read_lane(gi, kWave - 1);
+        e_base += read_lane(ei, kWave - 1);
+    }
+    t.count = k;
+    t.tau = T;
+    sort_pairs_and_write(t.key, t.ent, k, k, out);
 }
 
 // ---------------------------------------------------------------------------
