@@ -66,6 +66,16 @@ __device__ __forceinline__ int rank_below(uint64_t mask)
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 
+// The lane index as a value the compiler cannot hoist out of an enclosing
+// loop: code that derives many lane masks from it (sorting networks) keeps
+// them local instead of holding them in registers across the loop.
+__device__ __forceinline__ int opaque_lane()
+{
+    int l = lane();
+    __asm__ volatile("" : "+v"(l));
+    return l;
+}
+
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ uint32_t uniform_u(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
 

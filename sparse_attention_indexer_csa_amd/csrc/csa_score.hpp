@@ -48,18 +48,45 @@ struct RowOperand {
 
 // q_row = q + b*q_sb + i*q_ss, w_row = w + b*w_sb + i*w_ss.  Heads >= H get
 // weight zero and the (finite) queries of head H-1, so they add exact zeros.
-// Loads are issued unconditionally from clamped addresses so they can all be
-// in flight at once.
-// With full head blocks (H == 32*HB) no padding is applied, so nothing
-// consumes the loaded values before the first tile: the loads stay in flight
-// while the workgroup stages its first key tile.
+// Loads are issued unconditionally so they can all be in flight at once.
+// With full head blocks (H == 32*HB) and an 8-byte aligned weight row, a
+// lane's loads are one base address per head block with immediate offsets:
+// its 8-byte runs of 4 consecutive weights (heads 32hb + 8j + 4g .. +3) and
+// its 16-byte query fragments; nothing consumes them before the first
+// tile, so they stay in flight while the workgroup stages its first key tile.
 template <int HB, int KS>
 __device__ __forceinline__ void load_row(RowOperand<HB, KS> &r, const uint16_t *q_row, int64_t q_sh,
                                          const uint16_t *w_row, int H)
 {
-    const int l = lane();
+    // lane-derived addresses stay local to the call (see opaque_lane)
+    const int l = opaque_lane();
     const int n = l & 31, g = l >> 5;
-    const bool full = H == 32 * HB;
+    if (H == 32 * HB && (reinterpret_cast<uintptr_t>(w_row) & 7u) == 0) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            const uint16_t *p = q_row + (int64_t)(hb * 32 + n) * q_sh + 8 * g;
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                r.a[hb][s] = load_frag(p + 16 * s);
+        }
+        uint2 wv[HB][4];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                wv[hb][j] = *reinterpret_cast<const uint2 *>(w_row + hb * 32 + 8 * j + 4 * g);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // c_row(4j + c, g) = 8j + 4g + c
+                r.w[hb][4 * j + 0] = __uint_as_float(wv[hb][j].x << 16);
+                r.w[hb][4 * j + 1] = __uint_as_float(wv[hb][j].x & 0xFFFF0000u);
+                r.w[hb][4 * j + 2] = __uint_as_float(wv[hb][j].y << 16);
+                r.w[hb][4 * j + 3] = __uint_as_float(wv[hb][j].y & 0xFFFF0000u);
+            }
+        return;
+    }
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
         const int h = hb * 32 + n;
@@ -74,19 +101,11 @@ __device__ __forceinline__ void load_row(RowOperand<HB, KS> &r, const uint16_t *
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr)
             wb[hb][rr] = w_row[min(hb * 32 + c_row(rr, g), H - 1)];
-    if (full) {
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
-                r.w[hb][rr] = bf16_to_f32(wb[hb][rr]);
-    } else {
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
-                r.w[hb][rr] = (hb * 32 + c_row(rr, g) < H) ? bf16_to_f32(wb[hb][rr]) : 0.0f;
-    }
+        for (int rr = 0; rr < 16; ++rr)
+            r.w[hb][rr] = (hb * 32 + c_row(rr, g) < H) ? bf16_to_f32(wb[hb][rr]) : 0.0f;
 }
 
 // B fragments of 32 entries staged in LDS with a row pitch of `pitch`

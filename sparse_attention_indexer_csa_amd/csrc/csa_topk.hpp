@@ -421,9 +421,8 @@ __device__ __forceinline__ void bitonic_levels(uint64_t (&v)[E], int l)
 }
 
 template <int E>
-__device__ __forceinline__ void bitonic_sort_desc(uint64_t (&v)[E])
+__device__ __forceinline__ void bitonic_sort_desc(uint64_t (&v)[E], int l)
 {
-    const int l = lane();
     if constexpr (E <= 8) {
         bitonic_levels<E, 2>(v, l);
     } else {
@@ -451,7 +450,7 @@ __device__ __forceinline__ void bitonic_sort_desc(uint64_t (&v)[E])
 template <int E, typename EntT>
 __device__ __forceinline__ void sort_and_write(const uint32_t *key, const EntT *ent, int n, int k, int32_t *out)
 {
-    const int l = lane();
+    const int l = opaque_lane();
     uint64_t v[E];
 #pragma unroll
     for (int r = 0; r < E; ++r) {
@@ -459,7 +458,7 @@ __device__ __forceinline__ void sort_and_write(const uint32_t *key, const EntT *
         // ~entry in the low half: among equal keys the lower entry sorts first.
         v[r] = (e < n) ? (((uint64_t)key[e] << 32) | (uint32_t)~(uint32_t)ent[e]) : 0ull;
     }
-    bitonic_sort_desc<E>(v);
+    bitonic_sort_desc<E>(v, l);
 #pragma unroll
     for (int r = 0; r < E; ++r) {
         const int e = l * E + r;
@@ -530,7 +529,7 @@ template <int NR, typename EntT>
 __device__ __forceinline__ void topk_finish_regs(TopKRow<EntT> &t, int32_t *out)
 {
     static_assert(NR % 4 == 0, "four pairs per lane per group");
-    const int n = t.count, k = t.k, l = lane();
+    const int n = t.count, k = t.k, l = opaque_lane();
     wave_lds_fence();
     if (n <= k) {
         sort_pairs_and_write(t.key, t.ent, n, k, out);
