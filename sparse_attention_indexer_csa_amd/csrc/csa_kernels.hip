@@ -400,9 +400,81 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(const KernelAr
 }
 
 // ---------------------------------------------------------------------------
-// Row top-k for long rows: one workgroup per row; wave w streams the w-th
-// contiguous segment into its own buffer, then the waves select jointly.
+// Row top-k for long rows: one workgroup per row.  A first pass builds a
+// histogram of the row's keys by their top kCoarseBits bits and finds the
+// bucket holding the k-th largest key: every key below that bucket is beaten
+// by at least k others, so the waves start with tau just below it and their
+// buffers only ever see the few keys at or above it.  Wave w then streams
+// the w-th contiguous segment into its own buffer, and the waves select
+// jointly.
 // ---------------------------------------------------------------------------
+constexpr int kCoarseBits = 12;
+constexpr int kCoarseBins = 1 << kCoarseBits;
+
+// Key below which no key of the row can make its top k: one less than the
+// lower bound of the bucket that holds the k-th largest selectable key
+// (kKeyNegInf when the row has at most k of them).  All threads of the
+// workgroup call it; `hist` is kCoarseBins shared words, `part` NW+1.
+template <int NW>
+__device__ __forceinline__ uint32_t coarse_threshold(const float *src, int n, int k, uint32_t *hist, int *part)
+{
+    constexpr int kThreads = NW * kWave;
+    for (int b = threadIdx.x; b < kCoarseBins; b += kThreads)
+        hist[b] = 0u;
+    __syncthreads();
+    const int n4 = n / 4;
+    const float4 *src4 = reinterpret_cast<const float4 *>(src);
+    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
+    const int nv = vec ? n4 : 0;
+#pragma unroll 2
+    for (int i = threadIdx.x; i < nv; i += kThreads) {
+        const float4 v = src4[i];
+        const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t kv = score_key(f[c]);
+            if (key_selectable(kv))
+                atomicAdd(&hist[kv >> (32 - kCoarseBits)], 1u);
+        }
+    }
+    for (int j = nv * 4 + threadIdx.x; j < n; j += kThreads) {
+        const uint32_t kv = score_key(src[j]);
+        if (key_selectable(kv))
+            atomicAdd(&hist[kv >> (32 - kCoarseBits)], 1u);
+    }
+    __syncthreads();
+    // thread t owns bins kCoarseBins-1-t*P .. (descending), P bins each
+    constexpr int P = kCoarseBins / kThreads;
+    const int wv = threadIdx.x / kWave;
+    int h[P], tot = 0;
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+        h[r] = (int)hist[kCoarseBins - 1 - threadIdx.x * P - r];
+        tot += h[r];
+    }
+    const int incl = wave_inclusive_sum(tot);
+    if (lane() == kWave - 1)
+        part[wv] = incl;
+    __syncthreads();
+    int before = incl - tot;
+    for (int w = 0; w < wv; ++w)
+        before += part[w];
+    if (threadIdx.x == 0)
+        part[NW] = -1;
+    __syncthreads();
+    int cum = before;
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+        if (cum < k && k <= cum + h[r])
+            part[NW] = kCoarseBins - 1 - (int)threadIdx.x * P - r; // unique: cumulative counts are monotone
+        cum += h[r];
+    }
+    __syncthreads();
+    const int bin = part[NW];
+    __syncthreads();
+    return bin <= 0 ? kKeyNegInf : max(((uint32_t)bin << (32 - kCoarseBits)) - 1u, kKeyNegInf);
+}
+
 __global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(const KernelArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -415,6 +487,9 @@ __global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(con
     int *cnt = reinterpret_cast<int *>(ents + (size_t)kTopkBlockWaves * a.cap);  // [kTopkBlockWaves + 2]
     uint32_t *sel_key = reinterpret_cast<uint32_t *>(cnt + kTopkBlockWaves + 2);  // [top_k]
     uint32_t *sel_ent = sel_key + a.top_k;                              // [top_k]
+    // the coarse histogram reuses the wave buffers before they are filled
+    static_assert(kCoarseBins <= kTopkBlockWaves * (256 + 2 * 576), "coarse histogram fits the buffers");
+    const uint32_t tau0 = coarse_threshold<kTopkBlockWaves>(a.scores + row * a.W, n, a.top_k, hist_all, cnt);
 
     // segments of whole 64-entry chunks
     const int chunks = (n + kWave - 1) / kWave;
@@ -422,6 +497,7 @@ __global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(con
     const int j0 = min(wv * per * kWave, n), j1 = min((wv + 1) * per * kWave, n);
     TopKRow<uint32_t> tk;
     topk_init(tk, keys + (size_t)wv * a.cap, ents + (size_t)wv * a.cap, hist_all + wv * 256, a.cap, a.top_k);
+    tk.tau = tau0;
     if (j1 > j0)
         stream_row(tk, a.scores + row * a.W, j0, j1, n);
     topk_reduce(tk);

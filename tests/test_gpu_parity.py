@@ -130,6 +130,34 @@ def test_topk_exact_on_oracle_scores():
         np.testing.assert_array_equal(to_np(csa.topk(torch.from_numpy(s).cuda(), k)), oracle.topk(s, k), err_msg=f"k={k}")
 
 
+@pytest.mark.parametrize("dist", ["ties", "one_bucket", "gauss"])
+def test_topk_long_rows_exact(dist):
+    """Long rows (the workgroup-per-row kernel with its coarse-histogram
+    prefilter) stay exact: heavy ties, scores that all share one coarse bucket
+    (the prefilter cannot narrow them down), -inf/NaN holes, odd lengths."""
+    rng = np.random.default_rng(11)
+    W = 20000
+    if dist == "ties":
+        s = rng.integers(-3, 4, size=(9, W)).astype(np.float32)
+    elif dist == "one_bucket":
+        s = (1.0 + rng.random((9, W)) * 2.0 ** -10).astype(np.float32)
+    else:
+        s = rng.standard_normal((9, W)).astype(np.float32)
+    s[rng.random(s.shape) < 0.1] = -np.inf
+    s[rng.random(s.shape) < 0.01] = np.nan
+    s[1, :] = -np.inf
+    s[2, 100:] = -np.inf          # fewer valid entries than k
+    s[3, :] = 0.0                 # all ties
+    s[3, ::7] = -0.0
+    for k in (1, 512, 2048):
+        np.testing.assert_array_equal(to_np(csa.topk(torch.from_numpy(s).cuda(), k)), oracle.topk(s, k),
+                                      err_msg=f"{dist} k={k}")
+    # a row length that is not a multiple of 4 or of 64
+    s2 = np.ascontiguousarray(s[:, :W - 37])
+    np.testing.assert_array_equal(to_np(csa.topk(torch.from_numpy(s2).cuda(), 512)), oracle.topk(s2, 512),
+                                  err_msg=f"{dist} ragged")
+
+
 @pytest.mark.parametrize("name,plan", [("c2", "auto"), ("c4", "auto"), ("c5", "auto"), ("c5", "row_tiles")])
 def test_fused_select_equals_topk_of_scores(name, plan):
     P = make_config(name)
