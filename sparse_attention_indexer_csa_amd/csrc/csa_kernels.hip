@@ -283,16 +283,33 @@ void rows_kernel(const KernelArgs a)
 // ---------------------------------------------------------------------------
 // Split-row plan (long rows, few of them: decode).  Workgroup (row, chunk)
 // scores kSplitChunk consecutive entries of one row; each wave takes
-// kSplitTiles tiles of 64 entries and reads its keys straight from HBM (every
-// key byte is used by one row only, so there is nothing to share through
-// LDS).  Only the visible prefix of the row is read.  Scores go to a.scores
-// with row stride W; with full_rows the rest of the row is filled with -inf.
+// kSplitTiles tiles of 64 entries.  Every key byte is used by one row only,
+// so nothing is shared through LDS: each wave stages its own 32-entry
+// subtiles there by DMA (coalesced 16-byte slots, double-buffered, the next
+// subtile in flight while the current one is computed) and reads its MFMA
+// fragments back.  Only the visible prefix of the row is read (the DMA's
+// buffer resource ends there, so entries past it read zeros and are masked).
+// Scores go to a.scores with row stride W; with full_rows the rest of the row
+// is filled with -inf.
 // ---------------------------------------------------------------------------
+template <int D>
+struct SplitGeom {
+    static constexpr int kPitch = D + 8;                          // elements per LDS row
+    static constexpr int kRowChunks = kPitch / 8;                 // 16-byte slots per row
+    static constexpr int kSlots = 32 * kRowChunks;                // slots of one subtile
+    static constexpr int kDmaOps = (kSlots + kWave - 1) / kWave;  // DMA instructions per subtile
+    static constexpr int kBufBytes = kDmaOps * kWave * 16;        // subtile buffer (whole DMA ops)
+    static constexpr int kWaveBytes = 2 * kBufBytes;
+};
+
 template <int D, int HB>
 __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(const KernelArgs a)
 {
+    using G = SplitGeom<D>;
     constexpr int KS = D / 16;
     constexpr int kWaveEntries = kSplitTiles * kTileEntries;
+    constexpr int kSubtiles = 2 * kSplitTiles;
+    extern __shared__ __align__(16) unsigned char smem[];
     const int wv = uniform(threadIdx.x / kWave);
     const int l = lane();
     const int64_t row_id = blockIdx.x / a.n_chunks;
@@ -312,36 +329,67 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(const Kernel
     const int qseg = a.q_seg ? a.q_seg[row_id] : 0;
     const int32_t *kseg = a.k_seg ? a.k_seg + (int64_t)b * a.W : nullptr;
 
+    // subtile DMA: slot x*64 + l holds chunk slot % kRowChunks of entry
+    // slot / kRowChunks (slots past the 32 entries read zeros)
+    const int entry_bytes = (int)a.k_sw * 2;
+    const uint16_t *kb = a.k + b * a.k_sb;
+    unsigned char *wbuf = smem + (size_t)wv * G::kWaveBytes;
+    auto dma_subtile = [&](int sub) {
+        const int e0 = base + sub * 32;
+        const int n = max(0, min(32, thr - e0));
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(kb + (int64_t)e0 * a.k_sw, n * entry_bytes);
+        unsigned char *dst = wbuf + (sub & 1) * G::kBufBytes;
+#pragma unroll
+        for (int x = 0; x < G::kDmaOps; ++x) {
+            const int slot = x * kWave + l;
+            dma16(r, dst + x * kWave * 16,
+                  (uint32_t)((slot / G::kRowChunks) * entry_bytes + (slot % G::kRowChunks) * 16));
+        }
+    };
+    const int nsub = min(kSubtiles, (thr - base + 31) / 32);
+
+    dma_subtile(0);
     RowOperand<HB, KS> row;
     load_row<HB, KS>(row, a.q + b * a.q_sb + (int64_t)i * a.q_ss, a.q_sh, a.w + b * a.w_sb + (int64_t)i * a.w_ss, a.H);
-    const uint16_t *kb = a.k + b * a.k_sb;
 
+    float p0 = 0.0f;
 #pragma unroll 1
-    for (int t = 0; t < kSplitTiles; ++t) {
-        const int j0 = base + t * kTileEntries;
-        if (j0 >= thr && !a.full_rows)
-            break;
+    for (int sub = 0; sub < nsub; ++sub) {
+        wait_vm(); // this subtile's DMA (and, first time, the row operands)
+        bf16x8 bf[KS];
+        load_entries_lds<KS>(bf, reinterpret_cast<const uint16_t *>(wbuf + (sub & 1) * G::kBufBytes), 0, G::kPitch);
+        // the other buffer was read by the previous subtile, whose fragment
+        // reads completed before its MFMAs
+        if (sub + 1 < nsub)
+            dma_subtile(sub + 1);
+        const float p = subtile_partial<HB, KS>(row, bf);
+        if (sub & 1) {
+            const int j0 = base + (sub - 1) * 32;
+            const int j = j0 + l;
+            bool valid = j < thr;
+            if (kseg)
+                valid = valid && kseg[min(j, a.W - 1)] == qseg;
+            const float sc = scaled_score(combine_halves(p0, p), a.scale);
+            if (j < a.W && (a.full_rows || j < thr))
+                out[j] = valid ? sc : -INFINITY;
+        } else {
+            p0 = p;
+        }
+    }
+    if (nsub & 1) {
+        // odd count: the last 64-entry tile has only its first half computed
+        const int j0 = base + (nsub - 1) * 32;
         const int j = j0 + l;
         bool valid = j < thr;
         if (kseg)
-            valid = valid && kseg[j] == qseg;
-        bool do0, do1;
-        if (kseg) {
-            const uint64_t bal = ballot(valid);
-            do0 = (uint32_t)bal != 0u;
-            do1 = (uint32_t)(bal >> 32) != 0u;
-        } else {
-            do0 = j0 < thr;
-            do1 = j0 + 32 < thr;
-        }
-        float s = -INFINITY;
-        if (do0 || do1)
-            s = tile_scores<HB, KS>(row, do0, do1, a.scale, [&](bf16x8(&bf)[KS], int sub) {
-                load_entries_global<KS>(bf, kb, a.k_sw, j0 + sub * 32, thr);
-            });
+            valid = valid && kseg[min(j, a.W - 1)] == qseg;
+        const float sc = scaled_score(combine_halves(p0, 0.0f), a.scale);
         if (j < a.W && (a.full_rows || j < thr))
-            out[j] = valid ? s : -INFINITY;
+            out[j] = valid ? sc : -INFINITY;
     }
+    if (a.full_rows)
+        for (int j = base + ((nsub + 1) / 2) * kTileEntries + l; j < min(base + kWaveEntries, a.W); j += kWave)
+            out[j] = -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -576,10 +624,11 @@ template <int D>
 static hipError_t launch_split_d(int HB, const KernelArgs &a, hipStream_t s)
 {
     dim3 grid((unsigned)(a.rows * a.n_chunks)), block(kSplitWaves * kWave);
+    const size_t lds = (size_t)kSplitWaves * SplitGeom<D>::kWaveBytes;
     switch (HB) {
-    case 1: return launch(split_kernel<D, 1>, grid, block, 0, s, a);
-    case 2: return launch(split_kernel<D, 2>, grid, block, 0, s, a);
-    case 4: return launch(split_kernel<D, 4>, grid, block, 0, s, a);
+    case 1: return launch(split_kernel<D, 1>, grid, block, lds, s, a);
+    case 2: return launch(split_kernel<D, 2>, grid, block, lds, s, a);
+    case 4: return launch(split_kernel<D, 4>, grid, block, lds, s, a);
     default: return hipErrorInvalidValue;
     }
 }
