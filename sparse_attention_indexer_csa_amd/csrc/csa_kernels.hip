@@ -42,6 +42,17 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds, uint3
 // Waits for this wave's outstanding vector-memory operations (the tile DMA).
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Waits until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order), and for its LDS operations.
+template <int N>
+__device__ __forceinline__ void vm_wait_le()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Scores of the 64 entries j0 .. j0+63 of one row: lane l returns the
 // scaled score of entry j0 + l.  Subtiles (32 entries) flagged off are not
 // computed (their lanes return garbage that the caller masks).  `load(b, sub)`
@@ -312,12 +323,16 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(const Kernel
     extern __shared__ __align__(16) unsigned char smem[];
     const int wv = uniform(threadIdx.x / kWave);
     const int l = lane();
-    const int64_t row_id = blockIdx.x / a.n_chunks;
-    const int chunk = (int)(blockIdx.x % a.n_chunks);
+    // chunk-major order: every row's first chunks are dispatched before any
+    // row's last ones (which are empty for short rows), and the row of a
+    // given position rotates with the chunk so consecutive workgroups (which
+    // land on different XCDs) do not keep the same rows
+    const int64_t chunk = (int64_t)blockIdx.x / a.rows;
+    const int64_t row_id = ((int64_t)blockIdx.x % a.rows + chunk) % a.rows;
     const int b = (int)(row_id / a.S), i = (int)(row_id % a.S);
     const int64_t off = a.q_offset ? (int64_t)a.q_offset[b] : 0;
     const int thr = visible_entries(off + i, a.m, a.W);
-    const int base = chunk * kSplitChunk + wv * kWaveEntries;
+    const int base = (int)chunk * kSplitChunk + wv * kWaveEntries;
     float *out = a.scores + row_id * a.W;
 
     if (base >= thr) {
@@ -348,45 +363,66 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(const Kernel
     };
     const int nsub = min(kSubtiles, (thr - base + 31) / 32);
 
+    // Two subtiles stay in flight: a buffer is refilled as soon as its
+    // fragments are in registers.  Issue order per iteration s: the previous
+    // tile's score store (if any), then DMA(s+2), so when iteration s waits
+    // for DMA(s) the younger vector-memory ops are exactly DMA(s+1) and the
+    // store issued in iteration s-1, and the wait names that count.
+    auto score_store = [&](int tile_j0, float pa, float pb) {
+        const int j = tile_j0 + l;
+        bool valid = j < thr;
+        if (kseg)
+            valid = valid && kseg[min(j, a.W - 1)] == qseg;
+        const float sc = scaled_score(combine_halves(pa, pb), a.scale);
+        if (j < a.W && (a.full_rows || j < thr))
+            out[j] = valid ? sc : -INFINITY;
+    };
     dma_subtile(0);
     RowOperand<HB, KS> row;
     load_row<HB, KS>(row, a.q + b * a.q_sb + (int64_t)i * a.q_ss, a.q_sh, a.w + b * a.w_sb + (int64_t)i * a.w_ss, a.H);
+    if (nsub > 1)
+        dma_subtile(1);
 
-    float p0 = 0.0f;
+    float p0 = 0.0f, pend_a = 0.0f, pend_b = 0.0f;
+    bool pend = false;
 #pragma unroll 1
     for (int sub = 0; sub < nsub; ++sub) {
-        wait_vm(); // this subtile's DMA (and, first time, the row operands)
+        // wait for DMA(sub): younger ops are DMA(sub+1) (if issued) and the
+        // store of iteration sub-1 (if any)
+        // (with segments the store also loads segment ids: wait for all)
+        const bool younger_dma = sub + 1 < nsub && !kseg;
+        const bool younger_store = sub >= 3 && (sub & 1) == 1;
+        if (younger_dma && younger_store)
+            vm_wait_le<G::kDmaOps + 1>();
+        else if (younger_dma)
+            vm_wait_le<G::kDmaOps>();
+        else
+            wait_vm();
         bf16x8 bf[KS];
         load_entries_lds<KS>(bf, reinterpret_cast<const uint16_t *>(wbuf + (sub & 1) * G::kBufBytes), 0, G::kPitch);
-        // the other buffer was read by the previous subtile, whose fragment
-        // reads completed before its MFMAs
-        if (sub + 1 < nsub)
-            dma_subtile(sub + 1);
+        lds_wait();
+        __asm__ volatile("" ::: "memory");
+        if (pend) {
+            score_store(base + (sub - 2) * 32, pend_a, pend_b);
+            pend = false;
+        }
+        __asm__ volatile("" ::: "memory");
+        if (sub + 2 < nsub)
+            dma_subtile(sub + 2);
+        __asm__ volatile("" ::: "memory");
         const float p = subtile_partial<HB, KS>(row, bf);
         if (sub & 1) {
-            const int j0 = base + (sub - 1) * 32;
-            const int j = j0 + l;
-            bool valid = j < thr;
-            if (kseg)
-                valid = valid && kseg[min(j, a.W - 1)] == qseg;
-            const float sc = scaled_score(combine_halves(p0, p), a.scale);
-            if (j < a.W && (a.full_rows || j < thr))
-                out[j] = valid ? sc : -INFINITY;
+            pend_a = p0;
+            pend_b = p;
+            pend = true;
         } else {
             p0 = p;
         }
     }
-    if (nsub & 1) {
-        // odd count: the last 64-entry tile has only its first half computed
-        const int j0 = base + (nsub - 1) * 32;
-        const int j = j0 + l;
-        bool valid = j < thr;
-        if (kseg)
-            valid = valid && kseg[min(j, a.W - 1)] == qseg;
-        const float sc = scaled_score(combine_halves(p0, 0.0f), a.scale);
-        if (j < a.W && (a.full_rows || j < thr))
-            out[j] = valid ? sc : -INFINITY;
-    }
+    if (pend)
+        score_store(base + (nsub - 2) * 32, pend_a, pend_b);
+    if (nsub & 1) // the last 64-entry tile has only its first half computed
+        score_store(base + (nsub - 1) * 32, p0, 0.0f);
     if (a.full_rows)
         for (int j = base + ((nsub + 1) / 2) * kTileEntries + l; j < min(base + kWaveEntries, a.W); j += kWave)
             out[j] = -INFINITY;
