@@ -6,6 +6,8 @@ gpu_util).  Full-size workloads run in the launch configuration the benchmark
 times and are compared on sampled rows, which the oracle computes one by one.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -273,6 +275,34 @@ def test_widest_row_tile_cache(W, plans):
     if W > 65536:
         with pytest.raises(csa.CsaUnsupportedError):
             gpu_select(P, plan="row_tiles")
+
+
+@pytest.mark.parametrize("plan", PLANS)
+def test_chunked_prefill_equals_unchunked(plan):
+    """Chunked prefill through q_offset (each chunk of query rows passes its
+    absolute start position and the whole compressed cache) selects exactly
+    what the unchunked call selects for those rows, on Gaussian inputs: the
+    score of a pair does not depend on how the rows were batched."""
+    P = make_problem(2, 768, 64, 128, 192, 4, 64, dist="gauss", seed=31)
+    full = to_np(gpu_select(P, plan=plan)).reshape(P.B, P.S, -1)
+    for c0, c1 in ((0, 256), (256, 320), (320, 767), (767, 768)):
+        Pc = dataclasses.replace(P, S=c1 - c0, q=np.ascontiguousarray(P.q[:, :, c0:c1]),
+                                 w=np.ascontiguousarray(P.w[:, c0:c1]),
+                                 q_offset=np.full(P.B, c0, np.int32))
+        got = to_np(gpu_select(Pc, plan=plan)).reshape(P.B, c1 - c0, -1)
+        np.testing.assert_array_equal(got, full[:, c0:c1], err_msg=f"rows {c0}:{c1}")
+
+
+@pytest.mark.parametrize("dist", ["int", "gauss"])
+def test_compress_rate_one(dist):
+    """compress_rate = 1 (one compressed entry per token, W = S: the
+    uncompressed indexer): every plan against the oracle."""
+    P = make_problem(1, 1536, 64, 128, 1536, 1, 512, dist=dist, seed=41)
+    s_o, i_o = oracle.select(P)
+    for plan in PLANS:
+        idx, sc = gpu_select(P, plan=plan, return_scores=True)
+        assert_scores_close(to_np(sc).reshape(P.rows, P.W), s_o, exact=dist == "int", what=f"{dist} {plan}")
+        assert_topk_match(to_np(idx).reshape(P.rows, -1), i_o, s_o, exact=dist == "int", what=f"{dist} {plan}")
 
 
 def test_empty_batch_and_rows():
