@@ -46,9 +46,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
 // (0x007FFFFF, 0xFF800000], which is exactly the set of selectable keys.
 __device__ __forceinline__ uint32_t score_key(float s)
 {
+    // -0 becomes +0 (on the bits, so no float mode can touch denormals);
+    // negative floats then flip all bits, non-negative ones only the sign
     uint32_t u = __float_as_uint(s);
     u = (u == 0x80000000u) ? 0u : u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 constexpr uint32_t kKeyNegInf = 0x007FFFFFu;
@@ -56,7 +58,7 @@ constexpr uint32_t kKeyPosInf = 0xFF800000u;
 
 __device__ __forceinline__ bool key_selectable(uint32_t key) { return key > kKeyNegInf && key <= kKeyPosInf; }
 
-__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int rank_below(uint64_t mask)

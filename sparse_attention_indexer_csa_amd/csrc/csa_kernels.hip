@@ -442,11 +442,11 @@ __device__ __forceinline__ int row_length(const KernelArgs &a, int64_t row)
 }
 
 // Stream src[j0 .. j1) (j1 - j0 a multiple of 64 or the row end n) into the
-// wave's buffer, eight 64-entry chunks per batch of loads.
+// wave's buffer, sixteen 64-entry chunks per batch of loads.
 __device__ __forceinline__ void stream_row(TopKRow<uint32_t> &tk, const float *src, int j0, int j1, int n)
 {
     const int l = lane();
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 16;
 #pragma unroll 1
     for (int base = j0; base < j1; base += kBatch * kWave) {
         float v[kBatch];
@@ -495,38 +495,27 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(const KernelAr
 constexpr int kCoarseBits = 12;
 constexpr int kCoarseBins = 1 << kCoarseBits;
 
+template <int NW>
+__device__ __forceinline__ void coarse_clear(uint32_t *hist)
+{
+    for (int b = threadIdx.x; b < kCoarseBins; b += NW * kWave)
+        hist[b] = 0u;
+}
+
+__device__ __forceinline__ void coarse_add(uint32_t *hist, uint32_t kv)
+{
+    if (key_selectable(kv))
+        atomicAdd(&hist[kv >> (32 - kCoarseBits)], 1u);
+}
+
 // Key below which no key of the row can make its top k: one less than the
 // lower bound of the bucket that holds the k-th largest selectable key
-// (kKeyNegInf when the row has at most k of them).  All threads of the
-// workgroup call it; `hist` is kCoarseBins shared words, `part` NW+1.
+// (kKeyNegInf when the row has at most k of them), from a complete
+// histogram.  All threads of the workgroup call it; `part` is NW+1 words.
 template <int NW>
-__device__ __forceinline__ uint32_t coarse_threshold(const float *src, int n, int k, uint32_t *hist, int *part)
+__device__ __forceinline__ uint32_t coarse_find(const uint32_t *hist, int k, int *part)
 {
     constexpr int kThreads = NW * kWave;
-    for (int b = threadIdx.x; b < kCoarseBins; b += kThreads)
-        hist[b] = 0u;
-    __syncthreads();
-    const int n4 = n / 4;
-    const float4 *src4 = reinterpret_cast<const float4 *>(src);
-    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
-    const int nv = vec ? n4 : 0;
-#pragma unroll 2
-    for (int i = threadIdx.x; i < nv; i += kThreads) {
-        const float4 v = src4[i];
-        const float f[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t kv = score_key(f[c]);
-            if (key_selectable(kv))
-                atomicAdd(&hist[kv >> (32 - kCoarseBits)], 1u);
-        }
-    }
-    for (int j = nv * 4 + threadIdx.x; j < n; j += kThreads) {
-        const uint32_t kv = score_key(src[j]);
-        if (key_selectable(kv))
-            atomicAdd(&hist[kv >> (32 - kCoarseBits)], 1u);
-    }
-    __syncthreads();
     // thread t owns bins kCoarseBins-1-t*P .. (descending), P bins each
     constexpr int P = kCoarseBins / kThreads;
     const int wv = threadIdx.x / kWave;
@@ -559,6 +548,41 @@ __device__ __forceinline__ uint32_t coarse_threshold(const float *src, int n, in
     return bin <= 0 ? kKeyNegInf : max(((uint32_t)bin << (32 - kCoarseBits)) - 1u, kKeyNegInf);
 }
 
+// The same from the row in global memory (one read pass).
+template <int NW>
+__device__ __forceinline__ uint32_t coarse_threshold(const float *src, int n, int k, uint32_t *hist, int *part)
+{
+    constexpr int kThreads = NW * kWave;
+    coarse_clear<NW>(hist);
+    __syncthreads();
+    const int n4 = n / 4;
+    const float4 *src4 = reinterpret_cast<const float4 *>(src);
+    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
+    const int nv = vec ? n4 : 0;
+    // batches of 8 float4 per thread, all loads of a batch in flight at once
+    constexpr int kB = 8;
+#pragma unroll 1
+    for (int i0 = 0; i0 < nv; i0 += kB * kThreads) {
+        float4 v[kB];
+#pragma unroll
+        for (int x = 0; x < kB; ++x) {
+            const int i = i0 + x * kThreads + (int)threadIdx.x;
+            v[x] = i < nv ? src4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        }
+#pragma unroll
+        for (int x = 0; x < kB; ++x) {
+            coarse_add(hist, score_key(v[x].x));
+            coarse_add(hist, score_key(v[x].y));
+            coarse_add(hist, score_key(v[x].z));
+            coarse_add(hist, score_key(v[x].w));
+        }
+    }
+    for (int j = nv * 4 + threadIdx.x; j < n; j += kThreads)
+        coarse_add(hist, score_key(src[j]));
+    __syncthreads();
+    return coarse_find<NW>(hist, k, part);
+}
+
 __global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(const KernelArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -573,17 +597,61 @@ __global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(con
     uint32_t *sel_ent = sel_key + a.top_k;                              // [top_k]
     // the coarse histogram reuses the wave buffers before they are filled
     static_assert(kCoarseBins <= kTopkBlockWaves * (256 + 2 * 576), "coarse histogram fits the buffers");
-    const uint32_t tau0 = coarse_threshold<kTopkBlockWaves>(a.scores + row * a.W, n, a.top_k, hist_all, cnt);
-
     // segments of whole 64-entry chunks
     const int chunks = (n + kWave - 1) / kWave;
     const int per = (chunks + kTopkBlockWaves - 1) / kTopkBlockWaves;
     const int j0 = min(wv * per * kWave, n), j1 = min((wv + 1) * per * kWave, n);
+    const float *src = a.scores + row * a.W;
     TopKRow<uint32_t> tk;
-    topk_init(tk, keys + (size_t)wv * a.cap, ents + (size_t)wv * a.cap, hist_all + wv * 256, a.cap, a.top_k);
-    tk.tau = tau0;
-    if (j1 > j0)
-        stream_row(tk, a.scores + row * a.W, j0, j1, n);
+    {
+        const uint32_t tau0 = coarse_threshold<kTopkBlockWaves>(src, n, a.top_k, hist_all, cnt);
+        topk_init(tk, keys + (size_t)wv * a.cap, ents + (size_t)wv * a.cap, hist_all + wv * 256, a.cap, a.top_k);
+        tk.tau = tau0;
+        if (j1 > j0)
+            stream_row(tk, src, j0, j1, n);
+    }
+
+    // With the threshold preset the buffers usually end up holding a few
+    // hundred pairs in all: gather them (segments in wave order, so entry
+    // order) at the front and let one wave finish from registers.
+    if (lane() == 0)
+        cnt[wv] = tk.count;
+    __syncthreads();
+    int total = 0, before = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkBlockWaves; ++w) {
+        before += w < wv ? cnt[w] : 0;
+        total += cnt[w];
+    }
+    if (total <= 24 * kWave && a.cap * kTopkBlockWaves >= 24 * kWave) {
+        // two phases (read all, then write) since destinations overlap sources
+        constexpr int kMaxPer = 24; // >= cap / 64 whenever total fits
+        uint32_t kr[kMaxPer], er[kMaxPer];
+        const int mine = tk.count;
+#pragma unroll
+        for (int r = 0; r < kMaxPer; ++r) {
+            const int i = r * kWave + lane();
+            kr[r] = i < mine ? tk.key[i] : 0u;
+            er[r] = i < mine ? tk.ent[i] : 0u;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kMaxPer; ++r) {
+            const int i = r * kWave + lane();
+            if (i < mine) {
+                keys[before + i] = kr[r];
+                ents[before + i] = er[r];
+            }
+        }
+        __syncthreads();
+        if (wv == 0) {
+            TopKRow<uint32_t> all;
+            topk_init(all, keys, ents, hist_all, 24 * kWave, a.top_k);
+            all.count = total;
+            topk_finish_regs<24>(all, a.idx + row * a.top_k);
+        }
+        return;
+    }
     topk_reduce(tk);
     block_select_sort<kTopkBlockWaves>(keys, ents, a.cap, tk.count, a.top_k, hist_all, cnt, sel_key, sel_ent,
                                        a.idx + row * a.top_k);
