@@ -236,18 +236,20 @@ void rows_kernel(const KernelArgs a)
                 {
                     bf16x8 bf[KS];
                     load_entries_lds<KS>(bf, tile, 0, G::kPitch);
-                    p1 = logits_with_partial<HB, KS>(c0, row, bf, c1);
+                    p1 = logits_with_partial<HB, KS>(c0, row, bf, c1, [] {});
                 }
                 // combined unconditionally (a lane swap), so the epilogue
                 // above stays in the MFMA region instead of sinking into the
-                // branch
+                // branch; tile t-1's scores are emitted while the next
+                // subtile's first MFMAs run
                 const float prev_score = scaled_score(combine_halves(p0, p1), a.scale);
-                if (t > t_lo)
-                    emit(t - 1, prev_score, prev_valid);
                 {
                     bf16x8 bf[KS];
                     load_entries_lds<KS>(bf, tile, 32, G::kPitch);
-                    p0 = logits_with_partial<HB, KS>(c1, row, bf, c0);
+                    p0 = logits_with_partial<HB, KS>(c1, row, bf, c0, [&] {
+                        if (t > t_lo)
+                            emit(t - 1, prev_score, prev_valid);
+                    });
                 }
                 prev_valid = valid;
             }

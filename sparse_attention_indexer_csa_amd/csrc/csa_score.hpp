@@ -187,9 +187,9 @@ __device__ __forceinline__ float subtile_partial(const RowOperand<HB, KS> &r, co
 // max + fma work, which runs while the matrix core is busy.  Scheduling
 // fences keep that order.  The fma chains visit heads in the same order as
 // logits_partial(), so the partial is bit-identical to it.
-template <int HB, int KS>
+template <int HB, int KS, typename Mid>
 __device__ __forceinline__ float logits_with_partial(f32x16 (&cnew)[HB], const RowOperand<HB, KS> &r,
-                                                     const bf16x8 (&b)[KS], const f32x16 (&cold)[HB])
+                                                     const bf16x8 (&b)[KS], const f32x16 (&cold)[HB], Mid mid)
 {
     static_assert((HB * 16) % KS == 0, "epilogue must split evenly over the k-steps");
     constexpr int kPer = HB * 16 / KS;
@@ -204,6 +204,10 @@ __device__ __forceinline__ float logits_with_partial(f32x16 (&cnew)[HB], const R
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
             cnew[hb] = mfma32(r.a[hb][s], b[s], cnew[hb]);
+        // work handed in by the caller runs while the first k-step's MFMAs
+        // are in the pipe
+        if (s == 0)
+            mid();
 #pragma unroll
         for (int p = 0; p < kPer; ++p) {
             const int idx = s * kPer + p, hb = idx / 16, rr = idx % 16;
