@@ -469,22 +469,165 @@ __device__ __forceinline__ void sort_and_write(const uint32_t *key, const EntT *
         out[e] = -1;
 }
 
+// ---------------------------------------------------------------------------
+// Faster sort for buffers in which equal keys appear in entry order (every
+// buffer the top-k code sorts has that property): sort 32-bit composites
+// ((key - kmin) >> shift) << PB | (64E-1 - position) descending, where PB bits
+// hold the position and shift drops just enough low key bits to fit.  A
+// compare-exchange is then one v_med3_u32 against an all-ones / all-zeros
+// selector.  Equal keys order by position, i.e. by entry.  If dropping bits
+// made two different keys look equal, the result is discarded and the exact
+// 64-bit sort runs instead.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t med3u(uint32_t a, uint32_t b, uint32_t c)
+{
+    uint32_t r;
+    __asm__("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+template <int E, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic32_cross_levels(uint32_t (&v)[E], int l)
+{
+    if constexpr (STRIDE >= E && STRIDE >= 1) {
+        const int e = l * E;
+        const bool keep_max = ((e & STRIDE) == 0) == ((e & SIZE) == 0);
+        const uint32_t sel = keep_max ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+        for (int r = 0; r < E; ++r)
+            v[r] = med3u(v[r], lane_xor_u32<STRIDE / E>(v[r]), sel);
+        bitonic32_cross_levels<E, SIZE, STRIDE / 2>(v, l);
+    }
+}
+
+template <int E, int SIZE>
+__device__ __forceinline__ void bitonic32_in_lane(uint32_t (&v)[E], int l)
+{
+    // first element of a pair takes the max when its block sorts descending
+    const uint32_t sel = (((l * E) & SIZE) == 0) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int stride = (SIZE / 2 < E / 2 ? SIZE / 2 : E / 2); stride >= 1; stride >>= 1) {
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+            if ((r & stride) == 0) {
+                const uint32_t a = v[r], b = v[r + stride];
+                if constexpr (SIZE >= E) {
+                    v[r] = med3u(a, b, sel);
+                    v[r + stride] = med3u(a, b, ~sel);
+                } else if ((r & SIZE) == 0) {
+                    v[r] = max(a, b);
+                    v[r + stride] = min(a, b);
+                } else {
+                    v[r] = min(a, b);
+                    v[r + stride] = max(a, b);
+                }
+            }
+        }
+    }
+}
+
+template <int E, int SIZE>
+__device__ __forceinline__ void bitonic32_levels(uint32_t (&v)[E], int l)
+{
+    bitonic32_cross_levels<E, SIZE, SIZE / 2>(v, l);
+    bitonic32_in_lane<E, SIZE>(v, l);
+    if constexpr (SIZE < kWave * E)
+        bitonic32_levels<E, SIZE * 2>(v, l);
+}
+
+// Value of v in lane (lane + 1); lane 63 gets its own value.
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x130, 0xF, 0xF, false); // wave_shl:1
+}
+
+// Returns false (and writes nothing) when the truncated composites cannot
+// order the buffer exactly.
+template <int E, typename EntT>
+__device__ __forceinline__ bool sort_and_write_fast(const uint32_t *key, const EntT *ent, int n, int k, int32_t *out)
+{
+    constexpr int PB = (E == 1) ? 6 : (E == 2) ? 7 : (E == 4) ? 8 : 9;
+    static_assert((kWave * E) == (1 << PB), "position bits");
+    constexpr uint32_t kPosMask = (1u << PB) - 1u;
+    const int l = opaque_lane();
+    uint32_t kr[E];
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const int e = l * E + r;
+        kr[r] = e < n ? key[e] : 0u;
+        mn = e < n ? min(mn, kr[r]) : mn;
+        mx = max(mx, kr[r]);
+    }
+    mn = min(mn, lane_xor_u32<1>(mn));
+    mx = max(mx, lane_xor_u32<1>(mx));
+    mn = min(mn, lane_xor_u32<2>(mn));
+    mx = max(mx, lane_xor_u32<2>(mx));
+    mn = min(mn, lane_xor_u32<4>(mn));
+    mx = max(mx, lane_xor_u32<4>(mx));
+    mn = min(mn, lane_xor_u32<8>(mn));
+    mx = max(mx, lane_xor_u32<8>(mx));
+    mn = min(mn, lane_xor_u32<16>(mn));
+    mx = max(mx, lane_xor_u32<16>(mx));
+    mn = min(mn, lane_xor_u32<32>(mn));
+    mx = max(mx, lane_xor_u32<32>(mx));
+    const uint32_t kmin = uniform_u(mn), span = uniform_u(mx) - kmin;
+    const int bits = span ? 32 - __builtin_clz(span) : 0;
+    const int shift = bits > 32 - PB ? bits - (32 - PB) : 0;
+    uint32_t c[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const int e = l * E + r;
+        // empty slots are 0; a valid element has position bits >= 1 (e < n <= 64E)
+        c[r] = e < n ? (((kr[r] - kmin) >> shift) << PB) | (kPosMask - (uint32_t)e) : 0u;
+    }
+    bitonic32_levels<E, 2>(c, l);
+    if (shift > 0) {
+        // adjacent elements whose truncated keys are equal must have equal keys
+        bool bad = false;
+        const uint32_t next0 = from_next_lane(c[0]);
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+            const uint32_t a = c[r], b = (r + 1 < E) ? c[r + 1] : next0;
+            const bool pair_in = (r + 1 < E) || l + 1 < kWave;
+            if (pair_in && b != 0u && (a >> PB) == (b >> PB))
+                bad = bad || key[kPosMask - (a & kPosMask)] != key[kPosMask - (b & kPosMask)];
+        }
+        if (ballot(bad) != 0ull)
+            return false;
+    }
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const int e = l * E + r;
+        if (e < k)
+            out[e] = (e < n) ? (int32_t)ent[kPosMask - (c[r] & kPosMask)] : -1;
+    }
+    for (int e = kWave * E + l; e < k; e += kWave)
+        out[e] = -1;
+    return true;
+}
+
 template <typename EntT>
 __device__ __forceinline__ void sort_pairs_and_write(const uint32_t *key, const EntT *ent, int n, int k, int32_t *out)
 {
     wave_lds_fence();
-    if (n <= 64)
-        sort_and_write<1, EntT>(key, ent, n, k, out);
-    else if (n <= 128)
-        sort_and_write<2, EntT>(key, ent, n, k, out);
-    else if (n <= 256)
-        sort_and_write<4, EntT>(key, ent, n, k, out);
-    else if (n <= 512)
-        sort_and_write<8, EntT>(key, ent, n, k, out);
-    else if (n <= 1024)
+    if (n <= 64) {
+        if (!sort_and_write_fast<1, EntT>(key, ent, n, k, out))
+            sort_and_write<1, EntT>(key, ent, n, k, out);
+    } else if (n <= 128) {
+        if (!sort_and_write_fast<2, EntT>(key, ent, n, k, out))
+            sort_and_write<2, EntT>(key, ent, n, k, out);
+    } else if (n <= 256) {
+        if (!sort_and_write_fast<4, EntT>(key, ent, n, k, out))
+            sort_and_write<4, EntT>(key, ent, n, k, out);
+    } else if (n <= 512) {
+        if (!sort_and_write_fast<8, EntT>(key, ent, n, k, out))
+            sort_and_write<8, EntT>(key, ent, n, k, out);
+    } else if (n <= 1024) {
         sort_and_write<16, EntT>(key, ent, n, k, out);
-    else
+    } else {
         sort_and_write<32, EntT>(key, ent, n, k, out);
+    }
 }
 
 // Final selection of the row into out[0..k) (global memory).
