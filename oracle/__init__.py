@@ -57,6 +57,8 @@ def _load():
     lib.csa_oracle_valid.restype = None
     lib.csa_oracle_topk.argtypes = [i64, i64, i64, vp, vp]
     lib.csa_oracle_topk.restype = None
+    lib.csa_oracle_backward_f64.argtypes = [i64] * 6 + [f64] + [vp] * 13
+    lib.csa_oracle_backward_f64.restype = None
     lib.csa_oracle_version.restype = ctypes.c_int
     lib.csa_oracle_threads.restype = ctypes.c_int
     _lib = lib
@@ -143,3 +145,31 @@ def select(P, rows: Optional[Sequence[int]] = None):
     """(scores [n_rows, W] fp32, idx [n_rows, top_k] int32) of the given rows."""
     s = scores(P, rows)
     return s, topk(s, P.top_k)
+
+
+def backward(P, g: np.ndarray, bounds: bool = False):
+    """Gradients of sum(g * score) over unmasked (i, j), float64.
+
+    g is the upstream gradient of the scores, [B, S, W] float32 (its values at
+    masked positions are ignored).  Returns (dq [B,H,S,D], dk [B,W,D],
+    dw [B,S,H]); with bounds=True also (bq, bk, bw): per-element bounds on the
+    distance of a float32 implementation that rounds the gradient operand to
+    bf16 once (see csa_oracle.c).
+    """
+    _check(P)
+    gg = np.ascontiguousarray(g, dtype=np.float32)
+    if gg.shape != (P.B, P.S, P.W):
+        raise ValueError(f"g: expected {(P.B, P.S, P.W)}, got {gg.shape}")
+    lib = _load()
+    q, k, w = _c(P.q, np.uint16), _c(P.k, np.uint16), _c(P.w, np.uint16)
+    qo, qs, ks = _c(P.q_offset, np.int32), _c(P.q_seg, np.int32), _c(P.k_seg, np.int32)
+    dq = np.empty((P.B, P.H, P.S, P.D), np.float64)
+    dk = np.empty((P.B, P.W, P.D), np.float64)
+    dw = np.empty((P.B, P.S, P.H), np.float64)
+    bq = np.empty_like(dq) if bounds else None
+    bk = np.empty_like(dk) if bounds else None
+    bw = np.empty_like(dw) if bounds else None
+    lib.csa_oracle_backward_f64(P.B, P.S, P.H, P.D, P.W, P.m, float(P.scale), _ptr(q), _ptr(k), _ptr(w),
+                                _ptr(qo), _ptr(qs), _ptr(ks), _ptr(gg), _ptr(dq), _ptr(dk), _ptr(dw),
+                                _ptr(bq), _ptr(bk), _ptr(bw))
+    return (dq, dk, dw, bq, bk, bw) if bounds else (dq, dk, dw)

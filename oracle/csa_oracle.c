@@ -211,6 +211,135 @@ void csa_oracle_topk(int64_t rows, int64_t W, int64_t top_k, const float *scores
     }
 }
 
+/* One logit in float64, its sum of absolute products, and the float32 error
+ * bound eps_l on it (see csa_oracle_backward_f64). */
+static double logit_f64(const uint16_t *qr, const uint16_t *kr, int64_t D, double *eps_l)
+{
+    double logit = 0.0, mag = 0.0;
+    for (int64_t t = 0; t < D; ++t) {
+        double prod = (double)bf16_value(qr[t]) * (double)bf16_value(kr[t]);
+        logit = logit + prod;
+        mag = mag + fabs(prod);
+    }
+    *eps_l = 2.0 * (double)(D + 8) * ldexp(1.0, -24) * mag;
+    return logit;
+}
+
+/*
+ * Backward of the score (the vector-Jacobian product the custom VJP of
+ * MaxText PR #5079 "Add StreamIndex Kernel for CSA" returns, written out in
+ * closed form instead of differentiating a materialised [B,H,S,W] tensor, as
+ * the review of that backward asks).  For an upstream gradient g[b,i,j] of
+ * the scores, with l = sum_t q[b,h,i,t] k[b,j,t] and only unmasked (i, j)
+ * taking part (a masked score is a constant):
+ *
+ *   dw[b,i,h]   = scale * sum_j g[b,i,j] * ReLU(l)
+ *   dq[b,h,i,t] = scale * sum_j g[b,i,j] * w[b,i,h] * [l > 0] * k[b,j,t]
+ *   dk[b,j,t]   = scale * sum_i sum_h g[b,i,j] * w[b,i,h] * [l > 0] * q[b,h,i,t]
+ *
+ * ReLU's derivative at 0 is taken as 0, matching ReLU(l) = (l > 0 ? l : 0).
+ * Everything is accumulated in float64 in the order written.
+ *
+ * When the bound arrays are non-NULL the same loops also produce, per output
+ * element, a bound on how far a float32 implementation may lie from the
+ * float64 value:
+ *   - each logit computed in float32 is within eps_l = 2 (D+8) 2^-24
+ *     sum_t |q_t k_t| of l, so a term whose |l| <= eps_l has an undecided
+ *     [l > 0]: its full magnitude goes into the bound of dq and dk, and
+ *     |g| eps_l into the bound of dw;
+ *   - every other term may be off by rel = 2 (2^-9 + (n + 8) 2^-24) of its
+ *     magnitude, n the longest sum: the gradient operand rounded to bf16 once
+ *     (2^-9) plus float32 accumulation.
+ * dq/bq are [B,H,S,D], dk/bk [B,W,D], dw/bw [B,S,H]; g is [B,S,W] float32.
+ * The three bound arrays are all NULL or all set.
+ */
+void csa_oracle_backward_f64(int64_t B, int64_t S, int64_t H, int64_t D, int64_t W, int64_t m,
+                             double scale, const uint16_t *q, const uint16_t *k, const uint16_t *w,
+                             const int32_t *q_offset, const int32_t *q_seg, const int32_t *k_seg,
+                             const float *g, double *dq, double *dk, double *dw,
+                             double *bq, double *bk, double *bw)
+{
+    int64_t n_max = S * H > W ? S * H : W;
+    double rel = 2.0 * (ldexp(1.0, -9) + (double)(n_max + 8) * ldexp(1.0, -24));
+    double abs_scale = fabs(scale);
+
+    /* dq and dw: one query row at a time, entries j in order. */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t row = 0; row < B * S; ++row) {
+        int64_t b = row / S, i = row % S;
+        for (int64_t h = 0; h < H; ++h) {
+            const uint16_t *qr = &q[((b * H + h) * S + i) * D];
+            double wv = (double)bf16_value(w[(b * S + i) * H + h]);
+            double *dqr = &dq[((b * H + h) * S + i) * D];
+            double *bqr = bq ? &bq[((b * H + h) * S + i) * D] : NULL;
+            double dwv = 0.0, bwv = 0.0;
+            for (int64_t t = 0; t < D; ++t) {
+                dqr[t] = 0.0;
+                if (bqr)
+                    bqr[t] = 0.0;
+            }
+            for (int64_t j = 0; j < W; ++j) {
+                if (!entry_is_valid(b, i, j, S, W, m, q_offset, q_seg, k_seg))
+                    continue;
+                const uint16_t *kr = &k[(b * W + j) * D];
+                double gv = (double)g[(b * S + i) * W + j];
+                double eps_l;
+                double logit = logit_f64(qr, kr, D, &eps_l);
+                double relu = logit > 0.0 ? logit : 0.0;
+                dwv += scale * gv * relu;
+                bwv += abs_scale * fabs(gv) * (eps_l + rel * relu);
+                int undecided = fabs(logit) <= eps_l;
+                double c = scale * gv * wv;
+                for (int64_t t = 0; t < D; ++t) {
+                    double kv = (double)bf16_value(kr[t]);
+                    if (logit > 0.0)
+                        dqr[t] += c * kv;
+                    if (bqr)
+                        bqr[t] += (undecided ? 1.0 : rel) * fabs(c * kv);
+                }
+            }
+            dw[(b * S + i) * H + h] = dwv;
+            if (bw)
+                bw[(b * S + i) * H + h] = bwv;
+        }
+    }
+
+    /* dk: one entry at a time, rows i in order, heads h in order. */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t e = 0; e < B * W; ++e) {
+        int64_t b = e / W, j = e % W;
+        const uint16_t *kr = &k[(b * W + j) * D];
+        double *dkr = &dk[(b * W + j) * D];
+        double *bkr = bk ? &bk[(b * W + j) * D] : NULL;
+        for (int64_t t = 0; t < D; ++t) {
+            dkr[t] = 0.0;
+            if (bkr)
+                bkr[t] = 0.0;
+        }
+        for (int64_t i = 0; i < S; ++i) {
+            if (!entry_is_valid(b, i, j, S, W, m, q_offset, q_seg, k_seg))
+                continue;
+            double gv = (double)g[(b * S + i) * W + j];
+            for (int64_t h = 0; h < H; ++h) {
+                const uint16_t *qr = &q[((b * H + h) * S + i) * D];
+                double eps_l;
+                double logit = logit_f64(qr, kr, D, &eps_l);
+                int undecided = fabs(logit) <= eps_l;
+                if (!(logit > 0.0) && !(bkr && undecided))
+                    continue;
+                double c = scale * gv * (double)bf16_value(w[(b * S + i) * H + h]);
+                for (int64_t t = 0; t < D; ++t) {
+                    double qv = (double)bf16_value(qr[t]);
+                    if (logit > 0.0)
+                        dkr[t] += c * qv;
+                    if (bkr)
+                        bkr[t] += (undecided ? 1.0 : rel) * fabs(c * qv);
+                }
+            }
+        }
+    }
+}
+
 int csa_oracle_version(void) { return 1; }
 
 /* OpenMP threads the oracle's parallel loops use. */
