@@ -43,17 +43,21 @@ CSRC = os.path.join(ROOT, "sparse_attention_indexer_csa_amd", "csrc")
 # HBM bytes per launch of the fused prefill kernel, from FETCH_SIZE and
 # WRITE_SIZE counter runs scaled by what the same counters read for a plain
 # copy of known size.  Valid only for the kernel sources they were taken on
-# (sha256 over csrc/); reported as null otherwise.
+# (sha256 over the files the forward kernels are compiled from); reported as
+# null otherwise.
 MEASURED_TRAFFIC = {
-    "sources_sha": "0e8246d1abf866314d0658f1cacc1370eac0df629fd8a76eb2cb769fbaf84af2",
+    "sources_sha": "238a063a1e48818fd7115f61f3ccf23cb023fda2287e0452a32d086fd5854043",
     # FETCH_SIZE 139990 KiB x 1.99995 (copy calibration) + WRITE_SIZE 32768 KiB x 1.0
     "bytes_per_launch": 320_247_000,
 }
 
 
+FORWARD_SOURCES = ["csa_device.hpp", "csa_kernels.hip", "csa_launch.hpp", "csa_score.hpp", "csa_topk.hpp"]
+
+
 def sources_sha():
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(FORWARD_SOURCES):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
