@@ -127,6 +127,39 @@ csa_status csa_index_select(const csa_index_problem *p, const void *q, const voi
  * (0 when it needs none).  Host-only; checks the arguments like the call. */
 csa_status csa_index_workspace_size(const csa_index_problem *p, int32_t top_k, size_t *bytes);
 
+/*
+ * Backward of csa_index_score: the gradients of
+ *     L = sum over unmasked (b,i,j) of grad[b,i,j] * score[b,i,j]
+ * with respect to q, k and w (the vector-Jacobian product of the custom VJP
+ * in MaxText PR #5079 "Add StreamIndex Kernel for CSA"; its review asks for a
+ * fused backward that does not materialise the [B,H,S,W] per-head logits,
+ * and none is materialised here).  With l = q[b,h,i,:] . k[b,j,:]:
+ *     dw[b,i,h]   = scale * sum_j grad[b,i,j] * ReLU(l)
+ *     dq[b,h,i,:] = scale * w[b,i,h] * sum_j grad[b,i,j] * [l > 0] * k[b,j,:]
+ *     dk[b,j,:]   = scale * sum_i sum_h grad[b,i,j] * w[b,i,h] * [l > 0] * q[b,h,i,:]
+ * Masked pairs (the masks of csa_index_score) take no part: grad at masked
+ * positions is never read into a result and may hold anything finite or not.
+ * The ReLU derivative at l = 0 is 0.  Logits are recomputed exactly as the
+ * forward computes them; the gradient operands grad*[l>0] (for dq) and
+ * grad*w*[l>0] (for dk) are rounded to bf16 once and contracted with fp32
+ * accumulation; dw is an fp32 sum.
+ *
+ * grad: [B,S,W] fp32, dense.  Outputs are fp32, dense, every element written:
+ * dq [B,H,S,D] (4-byte aligned), dk [B,W,D] (16-byte aligned), dw [B,S,H]
+ * (4-byte aligned).  q, k, w, masks and the problem are as for
+ * csa_index_score (p->plan is not used).  workspace: at least
+ * csa_index_backward_workspace_size() bytes, 256-byte aligned (per-chunk
+ * partial key gradients); results do not depend on its prior contents and
+ * are deterministic.
+ */
+csa_status csa_index_score_backward(const csa_index_problem *p, const void *q, const void *k, const void *w,
+                                    const csa_index_masks *masks, const float *grad, float *dq, float *dk,
+                                    float *dw, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes csa_index_score_backward needs for this problem.  Host-only;
+ * checks the problem like the call. */
+csa_status csa_index_backward_workspace_size(const csa_index_problem *p, size_t *bytes);
+
 /* Plan the library would run for this problem (CSA_PLAN_ROW_TILES or
  * CSA_PLAN_SPLIT_ROWS), or -1 if the problem is invalid.  Host-only. */
 int32_t csa_index_resolve_plan(const csa_index_problem *p);

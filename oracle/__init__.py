@@ -59,6 +59,8 @@ def _load():
     lib.csa_oracle_topk.restype = None
     lib.csa_oracle_backward_f64.argtypes = [i64] * 6 + [f64] + [vp] * 13
     lib.csa_oracle_backward_f64.restype = None
+    lib.csa_oracle_backward_sample_f64.argtypes = [i64] * 6 + [f64] + [vp] * 7 + [i64, vp, i64, vp] + [vp] * 6
+    lib.csa_oracle_backward_sample_f64.restype = None
     lib.csa_oracle_version.restype = ctypes.c_int
     lib.csa_oracle_threads.restype = ctypes.c_int
     _lib = lib
@@ -173,3 +175,30 @@ def backward(P, g: np.ndarray, bounds: bool = False):
                                 _ptr(qo), _ptr(qs), _ptr(ks), _ptr(gg), _ptr(dq), _ptr(dk), _ptr(dw),
                                 _ptr(bq), _ptr(bk), _ptr(bw))
     return (dq, dk, dw, bq, bk, bw) if bounds else (dq, dk, dw)
+
+
+def backward_sample(P, g: np.ndarray, rows: Sequence[int], entries: Sequence[int]):
+    """The gradients of backward() for chosen rows (b*S+i) and entries (b*W+j):
+    (dq [n_rows,H,D], dw [n_rows,H], dk [n_entries,D], bq, bw, bk), float64,
+    with the same bounds."""
+    _check(P)
+    gg = np.ascontiguousarray(g, dtype=np.float32)
+    if gg.shape != (P.B, P.S, P.W):
+        raise ValueError(f"g: expected {(P.B, P.S, P.W)}, got {gg.shape}")
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    e = np.ascontiguousarray(np.asarray(entries, dtype=np.int64).reshape(-1))
+    if r.size and (r.min() < 0 or r.max() >= P.B * P.S):
+        raise ValueError("row id out of range")
+    if e.size and (e.min() < 0 or e.max() >= P.B * P.W):
+        raise ValueError("entry id out of range")
+    lib = _load()
+    q, k, w = _c(P.q, np.uint16), _c(P.k, np.uint16), _c(P.w, np.uint16)
+    qo, qs, ks = _c(P.q_offset, np.int32), _c(P.q_seg, np.int32), _c(P.k_seg, np.int32)
+    dq = np.empty((r.size, P.H, P.D), np.float64)
+    dw = np.empty((r.size, P.H), np.float64)
+    dk = np.empty((e.size, P.D), np.float64)
+    bq, bw, bk = np.empty_like(dq), np.empty_like(dw), np.empty_like(dk)
+    lib.csa_oracle_backward_sample_f64(P.B, P.S, P.H, P.D, P.W, P.m, float(P.scale), _ptr(q), _ptr(k), _ptr(w),
+                                       _ptr(qo), _ptr(qs), _ptr(ks), _ptr(gg), r.size, _ptr(r), e.size, _ptr(e),
+                                       _ptr(dq), _ptr(dw), _ptr(dk), _ptr(bq), _ptr(bw), _ptr(bk))
+    return dq, dw, dk, bq, bw, bk

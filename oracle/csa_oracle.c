@@ -253,91 +253,144 @@ static double logit_f64(const uint16_t *qr, const uint16_t *kr, int64_t D, doubl
  * dq/bq are [B,H,S,D], dk/bk [B,W,D], dw/bw [B,S,H]; g is [B,S,W] float32.
  * The three bound arrays are all NULL or all set.
  */
+/* dq [H][D] and dw [H] of query row (b, i), with bounds when bq != NULL. */
+static void backward_row(int64_t b, int64_t i, int64_t S, int64_t H, int64_t D, int64_t W, int64_t m,
+                         double scale, double rel, const uint16_t *q, const uint16_t *k, const uint16_t *w,
+                         const int32_t *q_offset, const int32_t *q_seg, const int32_t *k_seg, const float *g,
+                         double *dq, double *dw, double *bq, double *bw)
+{
+    for (int64_t h = 0; h < H; ++h) {
+        const uint16_t *qr = &q[((b * H + h) * S + i) * D];
+        double wv = (double)bf16_value(w[(b * S + i) * H + h]);
+        double *dqr = &dq[h * D];
+        double *bqr = bq ? &bq[h * D] : NULL;
+        double dwv = 0.0, bwv = 0.0;
+        for (int64_t t = 0; t < D; ++t) {
+            dqr[t] = 0.0;
+            if (bqr)
+                bqr[t] = 0.0;
+        }
+        for (int64_t j = 0; j < W; ++j) {
+            if (!entry_is_valid(b, i, j, S, W, m, q_offset, q_seg, k_seg))
+                continue;
+            const uint16_t *kr = &k[(b * W + j) * D];
+            double gv = (double)g[(b * S + i) * W + j];
+            double eps_l;
+            double logit = logit_f64(qr, kr, D, &eps_l);
+            double relu = logit > 0.0 ? logit : 0.0;
+            dwv += scale * gv * relu;
+            bwv += fabs(scale) * fabs(gv) * (eps_l + rel * relu);
+            int undecided = fabs(logit) <= eps_l;
+            double c = scale * gv * wv;
+            for (int64_t t = 0; t < D; ++t) {
+                double kv = (double)bf16_value(kr[t]);
+                if (logit > 0.0)
+                    dqr[t] += c * kv;
+                if (bqr)
+                    bqr[t] += (undecided ? 1.0 : rel) * fabs(c * kv);
+            }
+        }
+        dw[h] = dwv;
+        if (bw)
+            bw[h] = bwv;
+    }
+}
+
+/* dk [D] of entry (b, j): rows i in order, heads h in order. */
+static void backward_entry(int64_t b, int64_t j, int64_t S, int64_t H, int64_t D, int64_t W, int64_t m,
+                           double scale, double rel, const uint16_t *q, const uint16_t *k, const uint16_t *w,
+                           const int32_t *q_offset, const int32_t *q_seg, const int32_t *k_seg, const float *g,
+                           double *dk, double *bk)
+{
+    const uint16_t *kr = &k[(b * W + j) * D];
+    for (int64_t t = 0; t < D; ++t) {
+        dk[t] = 0.0;
+        if (bk)
+            bk[t] = 0.0;
+    }
+    for (int64_t i = 0; i < S; ++i) {
+        if (!entry_is_valid(b, i, j, S, W, m, q_offset, q_seg, k_seg))
+            continue;
+        double gv = (double)g[(b * S + i) * W + j];
+        for (int64_t h = 0; h < H; ++h) {
+            const uint16_t *qr = &q[((b * H + h) * S + i) * D];
+            double eps_l;
+            double logit = logit_f64(qr, kr, D, &eps_l);
+            int undecided = fabs(logit) <= eps_l;
+            if (!(logit > 0.0) && !(bk && undecided))
+                continue;
+            double c = scale * gv * (double)bf16_value(w[(b * S + i) * H + h]);
+            for (int64_t t = 0; t < D; ++t) {
+                double qv = (double)bf16_value(qr[t]);
+                if (logit > 0.0)
+                    dk[t] += c * qv;
+                if (bk)
+                    bk[t] += (undecided ? 1.0 : rel) * fabs(c * qv);
+            }
+        }
+    }
+}
+
+static double backward_rel(int64_t S, int64_t H, int64_t W)
+{
+    int64_t n_max = S * H > W ? S * H : W;
+    return 2.0 * (ldexp(1.0, -9) + (double)(n_max + 8) * ldexp(1.0, -24));
+}
+
 void csa_oracle_backward_f64(int64_t B, int64_t S, int64_t H, int64_t D, int64_t W, int64_t m,
                              double scale, const uint16_t *q, const uint16_t *k, const uint16_t *w,
                              const int32_t *q_offset, const int32_t *q_seg, const int32_t *k_seg,
                              const float *g, double *dq, double *dk, double *dw,
                              double *bq, double *bk, double *bw)
 {
-    int64_t n_max = S * H > W ? S * H : W;
-    double rel = 2.0 * (ldexp(1.0, -9) + (double)(n_max + 8) * ldexp(1.0, -24));
-    double abs_scale = fabs(scale);
-
-    /* dq and dw: one query row at a time, entries j in order. */
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t row = 0; row < B * S; ++row) {
-        int64_t b = row / S, i = row % S;
-        for (int64_t h = 0; h < H; ++h) {
-            const uint16_t *qr = &q[((b * H + h) * S + i) * D];
-            double wv = (double)bf16_value(w[(b * S + i) * H + h]);
-            double *dqr = &dq[((b * H + h) * S + i) * D];
-            double *bqr = bq ? &bq[((b * H + h) * S + i) * D] : NULL;
-            double dwv = 0.0, bwv = 0.0;
-            for (int64_t t = 0; t < D; ++t) {
-                dqr[t] = 0.0;
-                if (bqr)
-                    bqr[t] = 0.0;
-            }
-            for (int64_t j = 0; j < W; ++j) {
-                if (!entry_is_valid(b, i, j, S, W, m, q_offset, q_seg, k_seg))
-                    continue;
-                const uint16_t *kr = &k[(b * W + j) * D];
-                double gv = (double)g[(b * S + i) * W + j];
-                double eps_l;
-                double logit = logit_f64(qr, kr, D, &eps_l);
-                double relu = logit > 0.0 ? logit : 0.0;
-                dwv += scale * gv * relu;
-                bwv += abs_scale * fabs(gv) * (eps_l + rel * relu);
-                int undecided = fabs(logit) <= eps_l;
-                double c = scale * gv * wv;
+    double rel = backward_rel(S, H, W);
+#pragma omp parallel
+    {
+        double *rq = (double *)malloc(sizeof(double) * (size_t)(H * D));
+        double *rb = (double *)malloc(sizeof(double) * (size_t)(H * D));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t row = 0; row < B * S; ++row) {
+            int64_t b = row / S, i = row % S;
+            backward_row(b, i, S, H, D, W, m, scale, rel, q, k, w, q_offset, q_seg, k_seg, g, rq,
+                         &dw[row * H], bq ? rb : NULL, bw ? &bw[row * H] : NULL);
+            for (int64_t h = 0; h < H; ++h)
                 for (int64_t t = 0; t < D; ++t) {
-                    double kv = (double)bf16_value(kr[t]);
-                    if (logit > 0.0)
-                        dqr[t] += c * kv;
-                    if (bqr)
-                        bqr[t] += (undecided ? 1.0 : rel) * fabs(c * kv);
+                    dq[((b * H + h) * S + i) * D + t] = rq[h * D + t];
+                    if (bq)
+                        bq[((b * H + h) * S + i) * D + t] = rb[h * D + t];
                 }
-            }
-            dw[(b * S + i) * H + h] = dwv;
-            if (bw)
-                bw[(b * S + i) * H + h] = bwv;
         }
+        free(rq);
+        free(rb);
     }
-
-    /* dk: one entry at a time, rows i in order, heads h in order. */
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t e = 0; e < B * W; ++e) {
-        int64_t b = e / W, j = e % W;
-        const uint16_t *kr = &k[(b * W + j) * D];
-        double *dkr = &dk[(b * W + j) * D];
-        double *bkr = bk ? &bk[(b * W + j) * D] : NULL;
-        for (int64_t t = 0; t < D; ++t) {
-            dkr[t] = 0.0;
-            if (bkr)
-                bkr[t] = 0.0;
-        }
-        for (int64_t i = 0; i < S; ++i) {
-            if (!entry_is_valid(b, i, j, S, W, m, q_offset, q_seg, k_seg))
-                continue;
-            double gv = (double)g[(b * S + i) * W + j];
-            for (int64_t h = 0; h < H; ++h) {
-                const uint16_t *qr = &q[((b * H + h) * S + i) * D];
-                double eps_l;
-                double logit = logit_f64(qr, kr, D, &eps_l);
-                int undecided = fabs(logit) <= eps_l;
-                if (!(logit > 0.0) && !(bkr && undecided))
-                    continue;
-                double c = scale * gv * (double)bf16_value(w[(b * S + i) * H + h]);
-                for (int64_t t = 0; t < D; ++t) {
-                    double qv = (double)bf16_value(qr[t]);
-                    if (logit > 0.0)
-                        dkr[t] += c * qv;
-                    if (bkr)
-                        bkr[t] += (undecided ? 1.0 : rel) * fabs(c * qv);
-                }
-            }
-        }
-    }
+    for (int64_t e = 0; e < B * W; ++e)
+        backward_entry(e / W, e % W, S, H, D, W, m, scale, rel, q, k, w, q_offset, q_seg, k_seg, g,
+                       &dk[e * D], bk ? &bk[e * D] : NULL);
+}
+
+/*
+ * The same gradients for chosen query rows and entries only: dq [n_rows,H,D]
+ * and dw [n_rows,H] of rows[r] = b*S + i, dk [n_entries,D] of entries[e] =
+ * b*W + j, with bounds as above (all bound arrays NULL or all set).
+ */
+void csa_oracle_backward_sample_f64(int64_t B, int64_t S, int64_t H, int64_t D, int64_t W, int64_t m,
+                                    double scale, const uint16_t *q, const uint16_t *k, const uint16_t *w,
+                                    const int32_t *q_offset, const int32_t *q_seg, const int32_t *k_seg,
+                                    const float *g, int64_t n_rows, const int64_t *rows, int64_t n_entries,
+                                    const int64_t *entries, double *dq, double *dw, double *dk, double *bq,
+                                    double *bw, double *bk)
+{
+    (void)B;
+    double rel = backward_rel(S, H, W);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r)
+        backward_row(rows[r] / S, rows[r] % S, S, H, D, W, m, scale, rel, q, k, w, q_offset, q_seg, k_seg, g,
+                     &dq[r * H * D], &dw[r * H], bq ? &bq[r * H * D] : NULL, bw ? &bw[r * H] : NULL);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t e = 0; e < n_entries; ++e)
+        backward_entry(entries[e] / W, entries[e] % W, S, H, D, W, m, scale, rel, q, k, w, q_offset, q_seg,
+                       k_seg, g, &dk[e * D], bk ? &bk[e * D] : NULL);
 }
 
 int csa_oracle_version(void) { return 1; }

@@ -11,7 +11,9 @@ Entry points (same names as the C ABI):
 * :func:`score`  -> masked scores ``[B,S,W]`` fp32 (-inf where masked)
 * :func:`topk`   -> top-k indices of a score matrix
 * :func:`select` -> fused score + top-k, ``[B,S,top_k]`` int32 (optionally the scores)
-* :func:`workspace_size`, :func:`resolve_plan`
+* :func:`score_backward` -> ``(dq, dk, dw)`` fp32, the gradients of
+  ``sum(grad * score)`` over unmasked pairs
+* :func:`workspace_size`, :func:`backward_workspace_size`, :func:`resolve_plan`
 
 Tensor layouts: ``q [B,H,S,D]`` (any strides with D contiguous, e.g. a
 permuted view of a sequence-major ``[B,S,H,D]`` tensor), ``k [B,W,D]``,
@@ -67,6 +69,8 @@ SIGNATURES = {
     "csa_index_select": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "csa_index_workspace_size": (_I32, [_VP, _I32, ctypes.POINTER(_SZ)]),
     "csa_index_resolve_plan": (_I32, [_VP]),
+    "csa_index_score_backward": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "csa_index_backward_workspace_size": (_I32, [_VP, ctypes.POINTER(_SZ)]),
     "csa_status_string": (ctypes.c_char_p, [_I32]),
     "csa_last_error": (ctypes.c_char_p, []),
     "csa_index_abi_version": (_I32, []),
@@ -269,5 +273,60 @@ def select(q, k, w, top_k: int, compress_rate: int, scale: float = 1.0, q_offset
     return (out, sc) if return_scores else out
 
 
-__all__ = ["score", "topk", "select", "workspace_size", "resolve_plan", "load_library", "CsaIndexError",
+def backward_workspace_size(q, k, w, compress_rate: int) -> int:
+    """Bytes of workspace csa_index_score_backward needs for these tensors."""
+    lib = load_library()
+    p = _problem(q, k, w, compress_rate, 1.0, "auto")
+    n = ctypes.c_size_t(0)
+    st = lib.csa_index_backward_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    if st != _OK:
+        _raise(st, "csa_index_backward_workspace_size")
+    return n.value
+
+
+def score_backward(q, k, w, grad, compress_rate: int, scale: float = 1.0, q_offset=None, q_seg=None, k_seg=None,
+                   workspace: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
+                   dk: Optional[torch.Tensor] = None, dw: Optional[torch.Tensor] = None):
+    """Gradients (dq [B,H,S,D], dk [B,W,D], dw [B,S,H], fp32) of sum(grad * score)
+    over unmasked pairs (csa_index_score_backward); grad is [B,S,W] fp32."""
+    lib = load_library()
+    p = _problem(q, k, w, compress_rate, scale, "auto")
+    m = _masks(q, q_offset, q_seg, k_seg)
+    dev = q.device
+    _dev_tensor(grad, "grad", torch.float32, 3)
+    if tuple(grad.shape) != (p.B, p.S, p.W) or not grad.is_contiguous():
+        raise ValueError("grad must be a contiguous [B,S,W] float32 tensor")
+
+    def out(t, name, shape):
+        if t is None:
+            return torch.empty(shape, dtype=torch.float32, device=dev)
+        _dev_tensor(t, name, torch.float32, len(shape))
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shape}")
+        return t
+
+    dq = out(dq, "dq", (p.B, p.H, p.S, p.D))
+    dk = out(dk, "dk", (p.B, p.W, p.D))
+    dw = out(dw, "dw", (p.B, p.S, p.H))
+    need = ctypes.c_size_t(0)
+    st = lib.csa_index_backward_workspace_size(ctypes.byref(p), ctypes.byref(need))
+    if st != _OK:
+        _raise(st, "csa_index_backward_workspace_size")
+    ws = None
+    if need.value > 0:
+        if workspace is not None and workspace.is_cuda and workspace.numel() * workspace.element_size() >= need.value:
+            ws = workspace
+        else:
+            ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib.csa_index_score_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(w), ctypes.byref(m), _ptr(grad),
+                                      _ptr(dq), _ptr(dk), _ptr(dw), _ptr(ws), ws_bytes,
+                                      ctypes.c_void_p(_stream(dev)))
+    if st != _OK:
+        _raise(st, "csa_index_score_backward")
+    return dq, dk, dw
+
+
+__all__ = ["score", "topk", "select", "score_backward", "workspace_size", "backward_workspace_size",
+           "resolve_plan", "load_library", "CsaIndexError",
            "CsaUnsupportedError", "LIB_PATH", "SIGNATURES", "PLANS"]

@@ -12,6 +12,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -19,8 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcsa_index.so")
 
-SOURCES = ["csa_kernels.hip", "csa_api.cpp"]
-HEADERS = ["csa_device.hpp", "csa_score.hpp", "csa_topk.hpp", "csa_launch.hpp"]
+SOURCES = ["csa_kernels.hip", "csa_backward.hip", "csa_api.cpp"]
+HEADERS = ["csa_device.hpp", "csa_score.hpp", "csa_topk.hpp", "csa_launch.hpp", "csa_backward.hpp"]
 
 ARCH = os.environ.get("CSA_INDEX_ARCH", "gfx950")
 
@@ -32,34 +33,44 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set ROCM_PATH)")
 
 
-def command(out: str = LIB, extra: list | None = None) -> list:
-    return [
-        hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA accumulators in VGPRs: no AGPR <-> VGPR copies before the epilogue
-        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-        "-Wall", "-Wno-unused-function",
-        f"-I{INCLUDE}", f"-I{CSRC}",
-        *[os.path.join(CSRC, s) for s in SOURCES],
-        "-o", out, *(extra or []),
-    ]
+FLAGS = [
+    "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: no AGPR <-> VGPR copies before the epilogue
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    "-Wall", "-Wno-unused-function",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+NOISE = "'-packed-fp32-ops' is not a recognized feature"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always) and return its path."""
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = command(tmp)
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed to build libcsa_index.so")
-    noise = "'-packed-fp32-ops' is not a recognized feature"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if ln.strip() and noise not in ln]
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if ln.strip() and NOISE not in ln]
     if msgs and verbose:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (always, every source in parallel) and return its path."""
+    tag = f".tmp{os.getpid()}"
+    objs = [os.path.join(CSRC, s + tag + ".o") for s in SOURCES]
+    tmp = LIB + tag
+    try:
+        with ThreadPoolExecutor(len(SOURCES)) as ex:
+            list(ex.map(lambda so: _run([hipcc(), *FLAGS, "-c", os.path.join(CSRC, so[0]), "-o", so[1]], verbose),
+                        zip(SOURCES, objs)))
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

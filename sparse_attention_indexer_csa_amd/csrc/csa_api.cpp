@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <string>
 
+#include "csa_backward.hpp"
 #include "csa_launch.hpp"
 
 namespace {
@@ -214,6 +215,28 @@ size_t select_workspace(const csa_index_problem *p, const Checked &c)
     return (size_t)c.rows * (size_t)p->W * sizeof(float);
 }
 
+// Checks shared by the backward entry points.  The plan field is not used by
+// the backward, so it is read as AUTO.
+csa_status check_backward(const csa_index_problem *p, Checked &c, csa_index_problem &pa)
+{
+    if (!p)
+        return fail(CSA_ERR_INVALID_ARG, "problem descriptor is NULL");
+    pa = *p;
+    pa.plan = CSA_PLAN_AUTO;
+    csa_status st = check_problem(&pa, c);
+    if (st != CSA_OK)
+        return st;
+    const int rpw = 4 / c.HB;
+    const int64_t chunks = ((int64_t)pa.S + csa::kBwdChunkRows - 1) / csa::kBwdChunkRows;
+    const int64_t jtiles = ((int64_t)pa.W + csa::kBwdKeyTile - 1) / csa::kBwdKeyTile;
+    const int64_t rows_blocks = (int64_t)pa.B * ((pa.S + rpw - 1) / rpw);
+    const int64_t key_blocks = (int64_t)pa.B * 8 * ((chunks + 7) / 8) * jtiles;
+    const int64_t red_blocks = ((int64_t)pa.B * pa.W * pa.D / 4 + 255) / 256;
+    if (rows_blocks > 0x7FFFFFFF || key_blocks > 0x7FFFFFFF || red_blocks > 0x7FFFFFFF)
+        return fail(CSA_ERR_UNSUPPORTED, "problem too large for one backward launch");
+    return CSA_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -376,6 +399,85 @@ csa_status csa_index_select(const csa_index_problem *p, const void *q, const voi
         return st;
     a.scores = scores;
     return launched(csa::launch_rows(p->D, c.HB, mode, a, lds, s), "row-tile select");
+}
+
+csa_status csa_index_backward_workspace_size(const csa_index_problem *p, size_t *bytes)
+{
+    if (!bytes)
+        return fail(CSA_ERR_INVALID_ARG, "bytes is NULL");
+    Checked c;
+    csa_index_problem pa;
+    csa_status st = check_backward(p, c, pa);
+    if (st != CSA_OK)
+        return st;
+    *bytes = csa::bwd_workspace_bytes(pa.B, pa.S, pa.W, pa.D);
+    return ok();
+}
+
+csa_status csa_index_score_backward(const csa_index_problem *p, const void *q, const void *k, const void *w,
+                                    const csa_index_masks *masks, const float *grad, float *dq, float *dk,
+                                    float *dw, void *workspace, size_t workspace_bytes, void *stream)
+{
+    Checked c;
+    csa_index_problem pa;
+    csa_status st = check_backward(p, c, pa);
+    if (st != CSA_OK)
+        return st;
+    if ((st = check_inputs(&pa, c, q, k, w, masks)) != CSA_OK)
+        return st;
+    const int64_t nq = c.rows * pa.H, nk = (int64_t)pa.B * pa.W;
+    if (nq > 0 && (!dq || !dw || !aligned(dq, 4) || !aligned(dw, 4)))
+        return fail(CSA_ERR_INVALID_ARG, "dq and dw must be non-NULL, 4-byte aligned pointers");
+    if (nk > 0 && (!dk || !aligned(dk, 16)))
+        return fail(CSA_ERR_INVALID_ARG, "dk must be a non-NULL, 16-byte aligned pointer");
+    if (c.rows * pa.W > 0 && (!grad || !aligned(grad, 4)))
+        return fail(CSA_ERR_INVALID_ARG, "grad must be a non-NULL, 4-byte aligned pointer");
+    const size_t need = csa::bwd_workspace_bytes(pa.B, pa.S, pa.W, pa.D);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 256))
+            return fail(CSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    }
+    csa::BwdArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.w = static_cast<const uint16_t *>(w);
+    if (masks) {
+        a.q_offset = masks->q_offset;
+        a.q_seg = masks->q_seg;
+        a.k_seg = masks->k_seg;
+    }
+    a.g = grad;
+    a.dq = dq;
+    a.dk = dk;
+    a.dw = dw;
+    a.part = static_cast<float *>(workspace);
+    a.q_sb = pa.q_sb;
+    a.q_sh = pa.q_sh;
+    a.q_ss = pa.q_ss;
+    a.k_sb = pa.k_sb;
+    a.k_sw = pa.k_sw;
+    a.w_sb = pa.w_sb;
+    a.w_ss = pa.w_ss;
+    a.B = pa.B;
+    a.S = pa.S;
+    a.H = pa.H;
+    a.D = pa.D;
+    a.W = pa.W;
+    a.m = pa.compress_rate;
+    a.scale = pa.scale;
+    a.n_chunks = (pa.S + csa::kBwdChunkRows - 1) / csa::kBwdChunkRows;
+    a.n_jtiles = (pa.W + csa::kBwdKeyTile - 1) / csa::kBwdKeyTile;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = csa::launch_bwd_rows(pa.D, c.HB, a, s);
+    if (e != hipSuccess)
+        return launched(e, "backward dq/dw");
+    e = csa::launch_bwd_keys(pa.D, c.HB, a, s);
+    if (e != hipSuccess)
+        return launched(e, "backward dk partials");
+    return launched(csa::launch_bwd_reduce(a, s), "backward dk reduction");
 }
 
 } // extern "C"

@@ -1,0 +1,520 @@
+// Backward of the indexer score on MI355X (gfx950): the gradients of
+// L = sum over unmasked (i, j) of g[b,i,j] * score[b,i,j] with respect to q, k
+// and w, without the [B,H,S,W] per-head logits that differentiating the
+// score through autodiff materialises (MaxText PR #5079 "Add StreamIndex
+// Kernel for CSA", review of its custom VJP, which asks for a fused backward):
+//
+//   dw[b,i,h]   = scale * sum_j g[b,i,j] * ReLU(l)
+//   dq[b,h,i,:] = scale * w[b,i,h] * sum_j g[b,i,j] * [l > 0] * k[b,j,:]
+//   dk[b,j,:]   = scale * sum_i sum_h g[b,i,j] * w[b,i,h] * [l > 0] * q[b,h,i,:]
+//
+// with l = q[b,h,i,:] . k[b,j,:] recomputed per tile on MFMA exactly as the
+// forward computes it.  Masked pairs take no part (a masked score is a
+// constant).  The gradient operand of each product -- g [l>0] for dq,
+// g w [l>0] for dk -- is rounded to bf16 once (round to nearest even) and
+// contracted on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+//
+// Pass 1 (bwd_rows_kernel): a workgroup owns a few query rows, one wave per
+// (row, 32-head block); key tiles of 32 entries are staged in LDS and shared.
+// The transposed logits l[j, h] come out of the MFMA with one head per lane,
+// which is the layout the dq product needs for its A operand, so the
+// elementwise step stays in registers.  dw is a per-lane register sum.
+// Pass 2 (bwd_keys_kernel): a workgroup owns 128 entries (one wave per 32) and
+// a chunk of 256 rows; every row's q block and weights are staged in LDS and
+// the logits l[h, j] come out with one entry per lane, the layout of the dk
+// product's A operand.  Each (chunk, key tile) writes a partial to the
+// workspace; pass 3 (bwd_reduce_kernel) sums the partials of every chunk that
+// can see the tile, in chunk order, so results are deterministic.
+#include "csa_backward.hpp"
+#include "csa_score.hpp"
+
+namespace csa {
+
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = kBwdWaves * kWave;
+
+// fp32 rounded to the nearest bf16 (ties to even), returned as the fp32 with
+// the same value.  Inputs are finite.
+__device__ __forceinline__ float bf16_round(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return __uint_as_float(u & 0xFFFF0000u);
+}
+
+// Two bf16-valued floats packed into one dword: lo in bits 0-15, hi in 16-31.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// MFMA operand from eight bf16-valued floats (k index e = element e).
+__device__ __forceinline__ bf16x8 operand_from(const float (&v)[16], int base)
+{
+    u32x4 u;
+    u.x = pack_bf16(v[base + 0], v[base + 1]);
+    u.y = pack_bf16(v[base + 2], v[base + 3]);
+    u.z = pack_bf16(v[base + 4], v[base + 5]);
+    u.w = pack_bf16(v[base + 6], v[base + 7]);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// Eight bf16 values gathered from LDS as one MFMA operand.
+__device__ __forceinline__ bf16x8 gather8(const uint16_t *p, const int (&off)[8])
+{
+    u32x4 u;
+    u.x = (uint32_t)p[off[0]] | ((uint32_t)p[off[1]] << 16);
+    u.y = (uint32_t)p[off[2]] | ((uint32_t)p[off[3]] << 16);
+    u.z = (uint32_t)p[off[4]] | ((uint32_t)p[off[5]] << 16);
+    u.w = (uint32_t)p[off[6]] | ((uint32_t)p[off[7]] << 16);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ int64_t row_offset(const BwdArgs &a, int b)
+{
+    return a.q_offset ? (int64_t)a.q_offset[b] : 0;
+}
+
+// Whether any row of chunk c of batch b sees entry j0 (the first entry of a
+// key tile).  Visibility grows with the row, so the chunk's last row decides.
+// Both the key pass and the reduction use this, so a partial is read exactly
+// when it was written.
+__device__ __forceinline__ bool chunk_live(const BwdArgs &a, int b, int c, int j0)
+{
+    const int last = min((c + 1) * kBwdChunkRows, a.S) - 1;
+    return visible_entries(row_offset(a, b) + last, a.m, a.W) > j0;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: dq and dw.
+
+template <int D>
+struct RowTileGeom {
+    static constexpr int kPitch = D + 8;                  // LDS row pitch (elements)
+    static constexpr int kChunks = 32 * D / 8;            // 16-byte pieces per 32-entry tile
+    static constexpr int kPerThread = (kChunks + kBwdThreads - 1) / kBwdThreads;
+};
+
+template <int D, int HB>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_rows_kernel(const BwdArgs a)
+{
+    using G = RowTileGeom<D>;
+    constexpr int KS = D / 16, DB = D / 32, P = G::kPitch;
+    constexpr int RPW = kBwdWaves / HB; // query rows per workgroup
+    __shared__ __attribute__((aligned(16))) uint16_t tile[2][32 * P];
+
+    const int tid = threadIdx.x;
+    const int wv = uniform(tid / kWave);
+    const int l = lane(), n = l & 31, gi = l >> 5;
+    const int hb = wv % HB;
+    const int nrb = (a.S + RPW - 1) / RPW;
+    const int b = blockIdx.x / nrb;
+    // longest rows first
+    const int i0 = (nrb - 1 - (int)(blockIdx.x % nrb)) * RPW;
+    const int i = i0 + wv / HB;
+    const bool active = i < a.S;
+    const int64_t off = row_offset(a, b);
+    const int last = min(i0 + RPW, a.S) - 1;
+    const int ntiles = (visible_entries(off + last, a.m, a.W) + 31) / 32;
+    const int thr = active ? visible_entries(off + i, a.m, a.W) : 0;
+    const int qseg = (active && a.q_seg) ? a.q_seg[(int64_t)b * a.S + i] : 0;
+
+    // B operand of the transposed logits: this lane's head (32hb + n), eight
+    // values of D per k-step.  Heads past H read head H-1 (never written out).
+    bf16x8 qf[KS];
+    if (active) {
+        const uint16_t *qp = a.q + (int64_t)b * a.q_sb + (int64_t)min(32 * hb + n, a.H - 1) * a.q_sh +
+                             (int64_t)i * a.q_ss + 8 * gi;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            qf[s] = load_frag(qp + 16 * s);
+    } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            qf[s] = zero_frag();
+    }
+    const float *grow = a.g + ((int64_t)b * a.S + (active ? i : 0)) * a.W;
+    const uint16_t *kb = a.k + (int64_t)b * a.k_sb;
+
+    // LDS offsets of this lane's transposed key reads: entry 16jb + c_row(e, gi),
+    // column 32c + n.
+    int koff[2][8];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            koff[jb][e] = (16 * jb + c_row(e, gi)) * P + n;
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int c = 0; c < DB; ++c)
+        for (int r = 0; r < 16; ++r)
+            acc[c][r] = 0.0f;
+    float dw_acc = 0.0f;
+
+    uint4 pre[G::kPerThread];
+    auto fetch = [&](int t) {
+#pragma unroll
+        for (int u = 0; u < G::kPerThread; ++u) {
+            const int c = tid + u * kBwdThreads;
+            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+            const int j = 32 * t + row;
+            pre[u] = make_uint4(0, 0, 0, 0);
+            if (c < G::kChunks && j < a.W)
+                pre[u] = *reinterpret_cast<const uint4 *>(kb + (int64_t)j * a.k_sw + col);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < G::kPerThread; ++u) {
+            const int c = tid + u * kBwdThreads;
+            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+            if (c < G::kChunks)
+                *reinterpret_cast<uint4 *>(&tile[buf][row * P + col]) = pre[u];
+        }
+    };
+
+    if (ntiles > 0) {
+        fetch(0);
+        store(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles)
+            fetch(t + 1);
+        if (active && 32 * t < thr) {
+            const uint16_t *T = tile[t & 1];
+            // upstream gradient of this lane's 16 entries (0 where masked)
+            float ge[16], gb[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = 32 * t + c_row(r, gi);
+                const int jc = min(j, a.W - 1);
+                bool ok = j < thr;
+                if (a.k_seg)
+                    ok = ok && a.k_seg[(int64_t)b * a.W + jc] == qseg;
+                const float gv = grow[jc];
+                ge[r] = ok ? gv : 0.0f;
+                gb[r] = bf16_round(ge[r]);
+            }
+            // transposed logits: lane = head n of this block, register r = entry c_row(r, gi)
+            f32x16 lt;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                lt[r] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                lt = mfma32(load_frag(T + n * P + 16 * s + 8 * gi), qf[s], lt);
+            float pf[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float x = lt[r];
+                dw_acc = fmaf(ge[r], relu(x), dw_acc);
+                pf[r] = x > 0.0f ? gb[r] : 0.0f;
+            }
+            const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
+#pragma unroll
+            for (int c = 0; c < DB; ++c) {
+                acc[c] = mfma32(a0, gather8(T + 32 * c, koff[0]), acc[c]);
+                acc[c] = mfma32(a1, gather8(T + 32 * c, koff[1]), acc[c]);
+            }
+        }
+        if (t + 1 < ntiles)
+            store((t + 1) & 1);
+        __syncthreads();
+    }
+
+    // lanes n and n + 32 hold the same head over different entries
+    const float dw_sum = dw_acc + __shfl_xor(dw_acc, 32);
+    if (!active)
+        return;
+    const int hd = 32 * hb + n;
+    if (gi == 0 && hd < a.H)
+        a.dw[((int64_t)b * a.S + i) * a.H + hd] = a.scale * dw_sum;
+    const uint16_t *wrow = a.w + (int64_t)b * a.w_sb + (int64_t)i * a.w_ss;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int h = 32 * hb + c_row(r, gi);
+        if (h < a.H) {
+            const float f = a.scale * bf16_to_f32(wrow[h]);
+            float *dst = a.dq + (((int64_t)b * a.H + h) * a.S + i) * D + n;
+#pragma unroll
+            for (int c = 0; c < DB; ++c)
+                dst[32 * c] = f * acc[c][r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: per-chunk partial key gradients.
+
+template <int D, int HB>
+struct KeyGeom {
+    static constexpr int kPitch = D + 8;
+    static constexpr int kHeads = 32 * HB;
+    static constexpr int kChunks = kHeads * D / 8; // 16-byte pieces of one row's q block
+    static constexpr int kPerThread = (kChunks + kBwdThreads - 1) / kBwdThreads;
+    static constexpr size_t kQBytes = (size_t)kHeads * kPitch * 2;
+    static constexpr size_t kLdsBytes = 2 * kQBytes + 2 * (size_t)kHeads * 4;
+};
+
+template <int D, int HB>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_keys_kernel(const BwdArgs a)
+{
+    using G = KeyGeom<D, HB>;
+    constexpr int KS = D / 16, DB = D / 32, P = G::kPitch, NH = G::kHeads;
+    extern __shared__ __attribute__((aligned(16))) unsigned char bwd_smem[];
+    // two buffers of one row's q block [NH][P] bf16, then two of its weights [NH] fp32
+    auto qbuf = [&](int buf) { return reinterpret_cast<uint16_t *>(bwd_smem + buf * G::kQBytes); };
+    auto wbuf = [&](int buf) { return reinterpret_cast<float *>(bwd_smem + 2 * G::kQBytes + buf * NH * 4); };
+
+    // Workgroup -> (batch, chunk, key tile).  Workgroups are dealt to the 8
+    // XCDs in turn; XCD x takes every 8th chunk (latest rows first) with all
+    // of its key tiles in a row, so the tiles of one chunk run side by side on
+    // one XCD and share its L2 copy of the chunk's q rows.
+    const int per_b = 8 * ((a.n_chunks + 7) / 8) * a.n_jtiles;
+    const int b = blockIdx.x / per_b;
+    const int r_ = blockIdx.x % per_b;
+    const int x = r_ % 8, k_ = r_ / 8;
+    const int chunk = a.n_chunks - 1 - (8 * (k_ / a.n_jtiles) + x);
+    const int jt = k_ % a.n_jtiles;
+    if (chunk < 0)
+        return;
+    const int j0 = jt * kBwdKeyTile;
+    if (!chunk_live(a, b, chunk, j0))
+        return;
+    const int64_t off = row_offset(a, b);
+    const int c0 = chunk * kBwdChunkRows, c1 = min(c0 + kBwdChunkRows, a.S);
+    // first row that sees entry j0: (off + i + 1) div m > j0
+    const int64_t i_min = ((int64_t)j0 + 1) * a.m - 1 - off;
+    const int i_lo = (int)max((int64_t)c0, i_min);
+
+    const int tid = threadIdx.x;
+    const int wv = uniform(tid / kWave);
+    const int l = lane(), n = l & 31, gi = l >> 5;
+    const int jw = j0 + 32 * wv; // this wave's first entry
+    const int j = jw + n;        // this lane's entry (logit column, dk A row)
+    const bool wave_has = jw < a.W;
+
+    // B operand of the logits: this lane's entry, eight values of D per k-step.
+    bf16x8 kf[KS];
+    {
+        const uint16_t *kp = a.k + (int64_t)b * a.k_sb + (int64_t)min(j, a.W - 1) * a.k_sw + 8 * gi;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            kf[s] = j < a.W ? load_frag(kp + 16 * s) : zero_frag();
+    }
+    const int kseg = a.k_seg ? a.k_seg[(int64_t)b * a.W + min(j, a.W - 1)] : 0;
+
+    // LDS offsets of this lane's transposed q reads: head 16kb + c_row(e, gi),
+    // column n (plus 32hb heads and 32c columns).
+    int qoff[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            qoff[kb][e] = (16 * kb + c_row(e, gi)) * P + n;
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int c = 0; c < DB; ++c)
+        for (int r = 0; r < 16; ++r)
+            acc[c][r] = 0.0f;
+
+    uint4 pre[G::kPerThread];
+    float wpre = 0.0f, gpre = 0.0f;
+    int spre = 0;
+    auto fetch = [&](int i) {
+        const uint16_t *qrow = a.q + (int64_t)b * a.q_sb + (int64_t)i * a.q_ss;
+#pragma unroll
+        for (int u = 0; u < G::kPerThread; ++u) {
+            const int c = tid + u * kBwdThreads;
+            const int h = c / (D / 8), col = (c % (D / 8)) * 8;
+            pre[u] = make_uint4(0, 0, 0, 0);
+            if (c < G::kChunks && h < a.H)
+                pre[u] = *reinterpret_cast<const uint4 *>(qrow + (int64_t)h * a.q_sh + col);
+        }
+        if (tid < NH)
+            wpre = tid < a.H ? bf16_to_f32(a.w[(int64_t)b * a.w_sb + (int64_t)i * a.w_ss + tid]) : 0.0f;
+        gpre = a.g[((int64_t)b * a.S + i) * a.W + min(j, a.W - 1)];
+        spre = a.q_seg ? a.q_seg[(int64_t)b * a.S + i] : 0;
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < G::kPerThread; ++u) {
+            const int c = tid + u * kBwdThreads;
+            const int h = c / (D / 8), col = (c % (D / 8)) * 8;
+            if (c < G::kChunks)
+                *reinterpret_cast<uint4 *>(qbuf(buf) + h * P + col) = pre[u];
+        }
+        if (tid < NH)
+            wbuf(buf)[tid] = wpre;
+    };
+
+    fetch(i_lo);
+    store(0);
+    float gcur = gpre;
+    int scur = spre;
+    __syncthreads();
+    for (int i = i_lo; i < c1; ++i) {
+        const int buf = (i - i_lo) & 1;
+        const float g_i = gcur;
+        const int s_i = scur;
+        if (i + 1 < c1) {
+            fetch(i + 1);
+            gcur = gpre;
+            scur = spre;
+        }
+        const int thr = visible_entries(off + i, a.m, a.W);
+        bool ok = j < thr;
+        if (a.k_seg)
+            ok = ok && kseg == s_i;
+        const float ge = ok ? g_i : 0.0f;
+        if (wave_has && ballot(ok) != 0) {
+            const uint16_t *Q = qbuf(buf);
+            const float *Wt = wbuf(buf);
+            // rolled for two head blocks (fewer live registers), unrolled for four
+            constexpr int kHbUnroll = HB == 4 ? 4 : 1;
+#pragma unroll kHbUnroll
+            for (int hb = 0; hb < HB; ++hb) {
+                // logits: lane = entry n, register r = head 32hb + c_row(r, gi)
+                f32x16 lg;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    lg[r] = 0.0f;
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    lg = mfma32(load_frag(Q + (32 * hb + n) * P + 16 * s + 8 * gi), kf[s], lg);
+                float pf[16];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    // c_row(4 q4 + c, gi) = 8 q4 + 4 gi + c: four consecutive heads
+                    const float4 wq = *reinterpret_cast<const float4 *>(Wt + 32 * hb + 8 * q4 + 4 * gi);
+                    const float wr[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int r = 4 * q4 + c;
+                        pf[r] = lg[r] > 0.0f ? bf16_round(ge * wr[c]) : 0.0f;
+                    }
+                }
+                const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
+                const uint16_t *Qh = Q + 32 * hb * P;
+#pragma unroll
+                for (int c = 0; c < DB; ++c) {
+                    acc[c] = mfma32(a0, gather8(Qh + 32 * c, qoff[0]), acc[c]);
+                    acc[c] = mfma32(a1, gather8(Qh + 32 * c, qoff[1]), acc[c]);
+                }
+            }
+        }
+        if (i + 1 < c1)
+            store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // partial[b, chunk, entry, d]: lane = column 32c + n, register r = entry jw + c_row(r, gi)
+    float *dst = a.part + (((int64_t)b * a.n_chunks + chunk) * a.W) * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int je = jw + c_row(r, gi);
+        if (je < a.W) {
+#pragma unroll
+            for (int c = 0; c < DB; ++c)
+                dst[(int64_t)je * D + 32 * c + n] = acc[c][r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3: dk = scale * (sum of the live chunks' partials, in chunk order).
+
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a)
+{
+    const int D = a.D;
+    const int64_t per_b = (int64_t)a.W * D / 4;
+    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (v >= (int64_t)a.B * per_b)
+        return;
+    const int b = (int)(v / per_b);
+    const int64_t e = (v % per_b) * 4; // element within [W, D]
+    const int jtile0 = (int)(e / D) / kBwdKeyTile * kBwdKeyTile;
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int c = 0; c < a.n_chunks; ++c) {
+        if (!chunk_live(a, b, c, jtile0))
+            continue;
+        const float4 p = *reinterpret_cast<const float4 *>(a.part + (((int64_t)b * a.n_chunks + c) * a.W) * D + e);
+        s.x += p.x;
+        s.y += p.y;
+        s.z += p.z;
+        s.w += p.w;
+    }
+    float4 o = make_float4(a.scale * s.x, a.scale * s.y, a.scale * s.z, a.scale * s.w);
+    *reinterpret_cast<float4 *>(a.dk + (int64_t)b * a.W * D + e) = o;
+}
+
+template <int D, int HB>
+hipError_t launch_rows_t(const BwdArgs &a, hipStream_t s)
+{
+    constexpr int RPW = kBwdWaves / HB;
+    const int64_t blocks = (int64_t)a.B * ((a.S + RPW - 1) / RPW);
+    if (blocks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((bwd_rows_kernel<D, HB>), dim3((unsigned)blocks), dim3(kBwdThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D, int HB>
+hipError_t launch_keys_t(const BwdArgs &a, hipStream_t s)
+{
+    const int64_t blocks = (int64_t)a.B * 8 * ((a.n_chunks + 7) / 8) * a.n_jtiles;
+    if (blocks == 0)
+        return hipSuccess;
+    const size_t lds = KeyGeom<D, HB>::kLdsBytes;
+    auto kernel = bwd_keys_kernel<D, HB>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kBwdThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+} // namespace
+
+#define CSA_BWD_DISPATCH(FN, D, HB, ...)                                                                     \
+    switch ((D) * 10 + (HB)) {                                                                               \
+    case 321: return FN<32, 1>(__VA_ARGS__);                                                                 \
+    case 322: return FN<32, 2>(__VA_ARGS__);                                                                 \
+    case 324: return FN<32, 4>(__VA_ARGS__);                                                                 \
+    case 641: return FN<64, 1>(__VA_ARGS__);                                                                 \
+    case 642: return FN<64, 2>(__VA_ARGS__);                                                                 \
+    case 644: return FN<64, 4>(__VA_ARGS__);                                                                 \
+    case 1281: return FN<128, 1>(__VA_ARGS__);                                                               \
+    case 1282: return FN<128, 2>(__VA_ARGS__);                                                               \
+    case 1284: return FN<128, 4>(__VA_ARGS__);                                                               \
+    default: return hipErrorInvalidValue;                                                                    \
+    }
+
+hipError_t launch_bwd_rows(int D, int HB, const BwdArgs &a, hipStream_t s)
+{
+    CSA_BWD_DISPATCH(launch_rows_t, D, HB, a, s)
+}
+
+hipError_t launch_bwd_keys(int D, int HB, const BwdArgs &a, hipStream_t s)
+{
+    CSA_BWD_DISPATCH(launch_keys_t, D, HB, a, s)
+}
+
+hipError_t launch_bwd_reduce(const BwdArgs &a, hipStream_t s)
+{
+    const int64_t n = (int64_t)a.B * a.W * a.D / 4;
+    if (n == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+} // namespace csa

@@ -198,3 +198,39 @@ def test_binding_refuses_cpu_tensors():
         csa.select(q, k, w, 4, 4)
     with pytest.raises(ValueError):
         csa.topk(torch.zeros(2, 8), 2)
+
+
+def test_backward_workspace_and_validation(lib):
+    """The backward checks every pointer and the workspace on the host; an
+    empty batch succeeds without a launch."""
+    n = ctypes.c_size_t(0)
+    p = prob(B=2, S=600, H=4, D=32, W=40)
+    assert lib.csa_index_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == OK
+    assert n.value == 2 * 3 * 40 * 32 * 4  # B * ceil(S/256) row chunks * W * D fp32 partials
+    assert lib.csa_index_backward_workspace_size(ctypes.byref(prob(D=40)), ctypes.byref(n)) == UNSUPPORTED
+    assert lib.csa_index_backward_workspace_size(None, ctypes.byref(n)) == INVALID
+    # the plan field is not used by the backward
+    assert lib.csa_index_backward_workspace_size(ctypes.byref(prob(W=70000, plan=1)), ctypes.byref(n)) == OK
+
+    p = prob()
+    need = 16 * 8 * 4 * 1  # one chunk of W=8 entries x D=32
+    m = masks()
+
+    def call(q=FAKE, k=FAKE, w=FAKE, g=FAKE, dq=FAKE, dk=FAKE, dw=FAKE, ws=FAKE, wsb=need * 2, pp=p):
+        v = lambda x: ctypes.c_void_p(x) if x else None
+        return lib.csa_index_score_backward(ctypes.byref(pp), v(q), v(k), v(w), ctypes.byref(m), v(g), v(dq),
+                                            v(dk), v(dw), v(ws), wsb, None)
+
+    assert call(q=0) == INVALID
+    assert call(g=0) == INVALID
+    assert call(g=FAKE + 2) == INVALID
+    assert call(dq=0) == INVALID
+    assert call(dw=0) == INVALID
+    assert call(dk=0) == INVALID
+    assert call(dk=FAKE + 4) == INVALID  # dk must be 16-byte aligned
+    assert call(ws=0) == WORKSPACE
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=FAKE + 16) == INVALID
+    assert call(pp=prob(D=40)) == UNSUPPORTED
+    assert call(pp=prob(H=130)) == UNSUPPORTED
+    assert call(pp=prob(B=0), q=0, k=0, w=0, g=0, dq=0, dk=0, dw=0, ws=0, wsb=0) == OK

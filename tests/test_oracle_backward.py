@@ -171,3 +171,22 @@ def test_bounds_are_small_and_cover_undecided_signs():
     wv = float(_f64(P.w)[0, i, 0])
     expect = np.sum(np.abs(g[0, i, :nvis, None].astype(np.float64) * wv * kf), axis=0)
     np.testing.assert_allclose(bq[0, 0, i], expect, rtol=1e-12)
+
+
+def test_sampled_rows_and_entries_equal_the_full_backward():
+    """backward_sample (used at sizes where the full backward is too slow)
+    returns the full backward's values at the chosen rows and entries."""
+    P, g = _problem(16, segments="random", S=48)
+    dq, dk, dw, bq, bk, bw = oracle.backward(P, g, bounds=True)
+    rows = [0, 5, P.S + 47, 2 * P.S - 1]
+    ents = [0, 3, P.W + 11]
+    sq, sw, sk, sbq, sbw, sbk = oracle.backward_sample(P, g, rows, ents)
+    for r, row in enumerate(rows):
+        b, i = divmod(row, P.S)
+        np.testing.assert_array_equal(sq[r], dq[b, :, i, :])
+        np.testing.assert_array_equal(sw[r], dw[b, i])
+        np.testing.assert_array_equal(sbq[r], bq[b, :, i, :])
+    for e, ent in enumerate(ents):
+        b, j = divmod(ent, P.W)
+        np.testing.assert_array_equal(sk[e], dk[b, j])
+        np.testing.assert_array_equal(sbk[e], bk[b, j])
