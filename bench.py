@@ -14,6 +14,9 @@ Also reported on the same line:
   scores_only   csa_index_score on the same workload (fp32 [S,W] output)
   decode        B=64 one-row decode over a 32768-entry cache (valid length
                 U[4096,32768]): rows/s and HBM fraction of the algorithmic bytes
+  backward      csa_index_score_backward on the same workload (dq, dk, dw for a
+                Gaussian upstream gradient): algorithmic flops pairs * 6*H*D
+                (logit recompute, dq and dk products) over the call's duration
   cpu_baseline  the CPU oracle (scores + top-k) on a bounded sample of the rows
   copy          (leg "copy", off by default) a plain 1 GiB device copy, the
                 calibration kernel for the FETCH_SIZE / WRITE_SIZE counters
@@ -84,8 +87,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="select,score,decode,cpu",
-                    help="comma list of: select, score, decode, cpu, copy")
+    ap.add_argument("--legs", default="select,score,decode,backward,cpu",
+                    help="comma list of: select, score, decode, backward, cpu, copy")
     ap.add_argument("--cpu-row-stride", type=int, default=2,
                     help="the CPU baseline runs every n-th row of the prefill workload")
     return ap.parse_args()
@@ -227,6 +230,29 @@ def main():
                             "hbm_frac": gbs / PEAK_HBM_GBS,
                             "plan": csa.resolve_plan(dd["q"], dd["k"], dd["w"], Pd.m)}
         del caches, dd, ws
+
+    if "backward" in legs:
+        # gradient of sum(g * score) for a Gaussian upstream gradient g [B,S,W]
+        gen = torch.Generator(device=dev).manual_seed(13)
+        g = torch.randn((P.B, P.S, P.W), generator=gen, device=dev, dtype=torch.float32)
+        dq = torch.empty((P.B, P.H, P.S, P.D), dtype=torch.float32, device=dev)
+        dk = torch.empty((P.B, P.W, P.D), dtype=torch.float32, device=dev)
+        dw = torch.empty((P.B, P.S, P.H), dtype=torch.float32, device=dev)
+        wsb = torch.empty(csa.backward_workspace_size(d["q"], d["k"], d["w"], P.m), dtype=torch.uint8, device=dev)
+
+        def step_b(_):
+            csa.score_backward(d["q"], d["k"], d["w"], g, P.m, workspace=wsb, dq=dq, dk=dk, dw=dw)
+
+        log("backward leg")
+        wall, ev = time_calls(step_b, args.steps, args.warmup, torch)
+        bflops = pairs * 6 * P.H * P.D
+        ach = bflops / (ev * 1e-3) / 1e12
+        result["backward"] = {"workload": "gradients dq, dk, dw of sum(g * score) on " + CONFIG_TITLES["c3"],
+                              "entries_per_s": pairs / (wall * 1e-3), "ms_per_step": wall, "call_ms": ev,
+                              "flops_per_call": bflops, "tflops": ach, "mfma_frac": ach / PEAK_BF16_TFLOPS,
+                              "workspace_bytes": wsb.numel()}
+        log(f"backward: {wall:.3f} ms/step, call {ev:.3f} ms, {ach:.1f} TFLOP/s")
+        del g, dq, dk, dw, wsb
 
     if "copy" in legs:
         n = 1 << 30
