@@ -384,7 +384,18 @@ csa_status csa_index_select(const csa_index_problem *p, const void *q, const voi
         a.scores = buf;
         a.full_rows = scores ? 1 : 0;
         if (p->W > 0) {
-            hipError_t e = csa::launch_split(p->D, c.HB, a, s);
+            // without a score output only the visible prefixes are needed:
+            // few rows take the balanced split, others the chunked one
+            int cus = 0, dev = 0;
+            hipError_t e = hipGetDevice(&dev);
+            if (e == hipSuccess)
+                e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e != hipSuccess)
+                return fail(CSA_ERR_DEVICE, "cannot query the compute unit count");
+            if (!scores && c.rows <= csa::kStreamRows)
+                e = csa::launch_stream(p->D, c.HB, a, cus * csa::kStreamBlocksPerCU, s);
+            else
+                e = csa::launch_split(p->D, c.HB, a, s);
             if (e != hipSuccess)
                 return launched(e, "split score");
         }

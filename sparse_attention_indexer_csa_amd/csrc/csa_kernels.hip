@@ -431,6 +431,207 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(const Kernel
 }
 
 // ---------------------------------------------------------------------------
+// Balanced split plan (few rows, scores to the workspace: decode).  The
+// visible prefixes of all rows, cut into 64-entry tiles and laid end to end,
+// are divided into equal contiguous ranges, one per wave of a grid sized to
+// the chip, so every wave streams the same number of key bytes whatever the
+// row lengths are.  A wave walks its range tile by tile, crossing into the
+// next row where one ends (it then loads that row's query fragments and
+// weights); its key subtiles are staged by DMA exactly as in split_kernel,
+// two in flight.  Only visible entries are written.  Ranges are assigned so
+// that consecutive ranges (which mostly share a row) go to workgroups on the
+// same XCD.
+// ---------------------------------------------------------------------------
+constexpr int kStreamMaxRows = kStreamRows;
+
+template <int D, int HB>
+__global__ __launch_bounds__(kSplitWaves * kWave) void stream_kernel(const KernelArgs a)
+{
+    using G = SplitGeom<D>;
+    constexpr int KS = D / 16;
+    constexpr int kThreads = kSplitWaves * kWave;
+    constexpr int kPer = kStreamMaxRows / kThreads;
+    static_assert(kPer * kThreads == kStreamMaxRows, "rows per thread");
+    extern __shared__ __align__(16) unsigned char smem[];
+    int *pre = reinterpret_cast<int *>(smem + kSplitWaves * G::kWaveBytes); // [kStreamMaxRows + 1]
+    int *thr_of = pre + kStreamMaxRows + 1;                                // [kStreamMaxRows]
+    __shared__ int wsum[kSplitWaves];
+    const int tid = threadIdx.x;
+    const int wv = uniform(tid / kWave);
+    const int l = lane();
+    const int rows = (int)a.rows;
+
+    // tiles per row and their exclusive prefix (row-major order)
+    int cnt[kPer], tot = 0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int row = tid * kPer + r;
+        int t = 0;
+        if (row < rows) {
+            const int b = row / a.S, i = row % a.S;
+            t = visible_entries((a.q_offset ? (int64_t)a.q_offset[b] : 0) + i, a.m, a.W);
+            thr_of[row] = t;
+        }
+        cnt[r] = (t + kTileEntries - 1) / kTileEntries;
+        tot += cnt[r];
+    }
+    const int incl = wave_inclusive_sum(tot);
+    if (l == kWave - 1)
+        wsum[wv] = incl;
+    __syncthreads();
+    int before = incl - tot, total = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kSplitWaves; ++w2) {
+        before += w2 < wv ? wsum[w2] : 0;
+        total += wsum[w2];
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        pre[tid * kPer + r] = before;
+        before += cnt[r];
+    }
+    if (tid == 0)
+        pre[kStreamMaxRows] = total;
+    __syncthreads();
+
+    // this wave's range of tiles [t0, t1)
+    const int nblk = (int)gridDim.x;
+    const int blk = (nblk % 8 == 0) ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    const int64_t gw = (int64_t)blk * kSplitWaves + wv, nw = (int64_t)nblk * kSplitWaves;
+    const int t0 = (int)((int64_t)total * gw / nw), t1 = (int)((int64_t)total * (gw + 1) / nw);
+    if (t0 >= t1)
+        return;
+    // row holding tile t0: the last row r with pre[r] <= t0 (rows before it
+    // that have no tiles share its prefix and are passed over)
+    int lo = 0, hi = rows; // invariant: pre[lo] <= t0 < pre[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] <= t0)
+            lo = mid;
+        else
+            hi = mid;
+    }
+
+    // Cursor over tiles: row, first tile of the row, end of the row's tiles.
+    struct Cursor {
+        int row, rs, re;
+    };
+    auto next_row = [&](Cursor &c) {
+        do {
+            ++c.row;
+        } while (c.row < rows && pre[c.row + 1] == pre[c.row]);
+        c.rs = pre[c.row];
+        c.re = c.row < rows ? pre[c.row + 1] : c.rs;
+    };
+    Cursor dc{lo, pre[lo], pre[lo + 1]}; // DMA cursor (runs up to two subtiles ahead)
+    const int entry_bytes = (int)a.k_sw * 2;
+    unsigned char *wbuf = smem + (size_t)wv * G::kWaveBytes;
+    // DMA of subtile `sub` of this wave (tile t0 + sub/2); advances dc past
+    // the tile after its second half
+    auto dma_subtile = [&](int sub) {
+        const int t = t0 + (sub >> 1);
+        if (t >= dc.re)
+            next_row(dc);
+        const int b = dc.row / a.S;
+        const int e0 = (t - dc.rs) * kTileEntries + (sub & 1) * 32;
+        const int n = max(0, min(32, thr_of[dc.row] - e0));
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(a.k + b * a.k_sb + (int64_t)e0 * a.k_sw, n * entry_bytes);
+        unsigned char *dst = wbuf + (sub & 1) * G::kBufBytes;
+#pragma unroll
+        for (int x = 0; x < G::kDmaOps; ++x) {
+            const int slot = x * kWave + l;
+            dma16(r, dst + x * kWave * 16,
+                  (uint32_t)((slot / G::kRowChunks) * entry_bytes + (slot % G::kRowChunks) * 16));
+        }
+    };
+    const int nsub = 2 * (t1 - t0);
+    dma_subtile(0);
+    dma_subtile(1);
+
+    Cursor cc{lo - 1, 0, t0}; // compute cursor: entered its first row below
+    RowOperand<HB, KS> row;
+    int thr = 0, qseg = 0;
+    const int32_t *kseg = nullptr;
+    float *out = nullptr;
+    float p0 = 0.0f;
+    // pending store: the previous tile's partials and where they go
+    float pend_a = 0.0f, pend_b = 0.0f;
+    bool pend = false;
+    float *pend_out = nullptr;
+    int pend_j0 = 0, pend_thr = 0, pend_qseg = 0;
+    const int32_t *pend_kseg = nullptr;
+    auto score_store = [&](float *o, int j0, int th, const int32_t *ks, int qs, float pa, float pb) {
+        const int j = j0 + l;
+        bool valid = j < th;
+        if (ks)
+            valid = valid && ks[min(j, a.W - 1)] == qs;
+        const float sc = scaled_score(combine_halves(pa, pb), a.scale);
+        if (j < th)
+            o[j] = valid ? sc : -INFINITY;
+    };
+    const bool segs = a.k_seg != nullptr;
+#pragma unroll 1
+    for (int sub = 0; sub < nsub; ++sub) {
+        const int t = t0 + (sub >> 1);
+        bool switched = false;
+        if ((sub & 1) == 0 && t >= cc.re) {
+            next_row(cc);
+            switched = true;
+        }
+        if (switched) {
+            // new row: its operands, then everything outstanding
+            const int b = cc.row / a.S, i = cc.row % a.S;
+            load_row<HB, KS>(row, a.q + b * a.q_sb + (int64_t)i * a.q_ss, a.q_sh,
+                             a.w + b * a.w_sb + (int64_t)i * a.w_ss, a.H);
+            thr = thr_of[cc.row];
+            kseg = segs ? a.k_seg + (int64_t)b * a.W : nullptr;
+            qseg = segs ? a.q_seg[cc.row] : 0;
+            out = a.scores + (int64_t)cc.row * a.W;
+            wait_vm();
+        } else {
+            // younger vector-memory ops than DMA(sub): DMA(sub+1) if issued,
+            // and the store issued in the previous iteration if any (stores
+            // go out in even iterations from the fourth subtile on)
+            const bool younger_dma = sub + 1 < nsub && !segs;
+            const bool younger_store = sub >= 3 && (sub & 1) == 1;
+            if (younger_dma && younger_store)
+                vm_wait_le<G::kDmaOps + 1>();
+            else if (younger_dma)
+                vm_wait_le<G::kDmaOps>();
+            else
+                wait_vm();
+        }
+        bf16x8 bf[KS];
+        load_entries_lds<KS>(bf, reinterpret_cast<const uint16_t *>(wbuf + (sub & 1) * G::kBufBytes), 0, G::kPitch);
+        lds_wait();
+        __asm__ volatile("" ::: "memory");
+        if (pend) {
+            score_store(pend_out, pend_j0, pend_thr, pend_kseg, pend_qseg, pend_a, pend_b);
+            pend = false;
+        }
+        __asm__ volatile("" ::: "memory");
+        if (sub + 2 < nsub)
+            dma_subtile(sub + 2);
+        __asm__ volatile("" ::: "memory");
+        const float p = subtile_partial<HB, KS>(row, bf);
+        if (sub & 1) {
+            pend_a = p0;
+            pend_b = p;
+            pend = true;
+            pend_out = out;
+            pend_j0 = (t - cc.rs) * kTileEntries;
+            pend_thr = thr;
+            pend_kseg = kseg;
+            pend_qseg = qseg;
+        } else {
+            p0 = p;
+        }
+    }
+    if (pend)
+        score_store(pend_out, pend_j0, pend_thr, pend_kseg, pend_qseg, pend_a, pend_b);
+}
+
+// ---------------------------------------------------------------------------
 // Row top-k over a dense fp32 score matrix, one wave per row (short rows).
 // With limit_rows the row ends at its visible prefix (q_offset, m).
 // ---------------------------------------------------------------------------
@@ -745,6 +946,31 @@ hipError_t launch_split(int D, int HB, const KernelArgs &a, hipStream_t s)
     case 32: return launch_split_d<32>(HB, a, s);
     case 64: return launch_split_d<64>(HB, a, s);
     case 128: return launch_split_d<128>(HB, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int D>
+static hipError_t launch_stream_d(int HB, const KernelArgs &a, int blocks, hipStream_t s)
+{
+    dim3 grid((unsigned)blocks), block(kSplitWaves * kWave);
+    const size_t lds = (size_t)kSplitWaves * SplitGeom<D>::kWaveBytes + (2 * kStreamMaxRows + 1) * sizeof(int);
+    switch (HB) {
+    case 1: return launch(stream_kernel<D, 1>, grid, block, lds, s, a);
+    case 2: return launch(stream_kernel<D, 2>, grid, block, lds, s, a);
+    case 4: return launch(stream_kernel<D, 4>, grid, block, lds, s, a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_stream(int D, int HB, const KernelArgs &a, int blocks, hipStream_t s)
+{
+    if (a.rows > kStreamMaxRows)
+        return hipErrorInvalidValue;
+    switch (D) {
+    case 32: return launch_stream_d<32>(HB, a, blocks, s);
+    case 64: return launch_stream_d<64>(HB, a, blocks, s);
+    case 128: return launch_stream_d<128>(HB, a, blocks, s);
     default: return hipErrorInvalidValue;
     }
 }

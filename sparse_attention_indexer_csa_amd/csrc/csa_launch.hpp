@@ -38,6 +38,9 @@ constexpr int kTileEntries = 64;        // compressed entries per LDS K tile
 constexpr int kSplitWaves = 4;
 constexpr int kSplitTiles = 4;          // 64-entry tiles per wave
 constexpr int kSplitChunk = kSplitWaves * kSplitTiles * kTileEntries;
+// Balanced split plan: rows it takes, workgroups per compute unit.
+constexpr int kStreamRows = 256;
+constexpr int kStreamBlocksPerCU = 2;
 // Top-k kernel geometry: one wave per row, or one workgroup per long row.
 constexpr int kTopkWaves = 4;
 constexpr int kTopkBlockWaves = 8;
@@ -64,6 +67,9 @@ size_t topk_block_lds_bytes(int cap, int top_k);
 // Each returns hipSuccess or the launch error; nothing is synchronised.
 hipError_t launch_rows(int D, int HB, int mode, const KernelArgs &a, size_t lds, hipStream_t s);
 hipError_t launch_split(int D, int HB, const KernelArgs &a, hipStream_t s);
+// Balanced split over `blocks` workgroups; rows <= kStreamRows, scores of the
+// visible prefixes only.
+hipError_t launch_stream(int D, int HB, const KernelArgs &a, int blocks, hipStream_t s);
 hipError_t launch_topk(const KernelArgs &a, size_t lds, hipStream_t s);
 hipError_t launch_topk_block(const KernelArgs &a, size_t lds, hipStream_t s);
 

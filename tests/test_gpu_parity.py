@@ -253,6 +253,9 @@ def test_edge_shapes_exact(case, plan):
     s_o, i_o = oracle.select(P)
     idx, sc = gpu_select(P, plan=plan, return_scores=True)
     assert_topk_match(to_np(idx).reshape(P.rows, -1), i_o, s_o, exact=True, what=str(case))
+    # without a score output the split plan takes its balanced kernel
+    assert_topk_match(to_np(gpu_select(P, plan=plan)).reshape(P.rows, -1), i_o, s_o, exact=True,
+                      what=f"{case} select only")
     if W > 0:
         assert_scores_close(to_np(sc).reshape(P.rows, W), s_o, exact=True, what=str(case))
         assert_scores_close(to_np(gpu_score(P, plan=plan)).reshape(P.rows, W), s_o, exact=True, what=str(case))
@@ -335,3 +338,29 @@ def test_sequence_major_q_and_padded_k_rows():
     i2, s2 = gpu_select(P, dev=d2, return_scores=True)
     np.testing.assert_array_equal(to_np(i2), to_np(ref_i))
     assert np.array_equal(to_np(s2).view(np.uint32), to_np(ref_s).view(np.uint32))
+
+
+BALANCED = [
+    # B, S, H, D, W, m, top_k, lengths lo..hi, segments
+    (256, 1, 64, 128, 4096, 4, 512, (0, 4096), None),    # most rows the balanced split takes, empty rows among them
+    (37, 1, 32, 64, 2500, 4, 100, (1, 2500), None),      # ragged tails, one head block
+    (5, 40, 16, 32, 3000, 2, 64, None, "random"),        # several rows per sequence, segments
+    (3, 1, 128, 128, 9000, 4, 2048, (8000, 9000), None), # four head blocks, top_k = 2048
+]
+
+
+@pytest.mark.parametrize("case", BALANCED, ids=[str(c[:7]) for c in BALANCED])
+def test_balanced_split_exact(case):
+    """The split plan without a score output divides the rows' visible
+    entries evenly over the waves (ranges cross row ends); every selection
+    equals the oracle's on the integer grid, and equals the chunked kernel's
+    (the select with a score output) bit for bit."""
+    B, S, H, D, W, m, k, lens, segs = case
+    P = make_problem(B, S, H, D, W, m, k, dist="int", seed=sum(case[:7]), decode_lengths=lens,
+                     segments=segs)
+    d = dev_problem(P)
+    s_o, i_o = oracle.select(P)
+    idx = to_np(gpu_select(P, plan="split_rows", dev=d)).reshape(P.rows, -1)
+    assert_topk_match(idx, i_o, s_o, exact=True, what=f"{case}")
+    idx2, _ = gpu_select(P, plan="split_rows", dev=d, return_scores=True)
+    np.testing.assert_array_equal(to_np(idx2).reshape(P.rows, -1), idx)
