@@ -21,7 +21,12 @@ Also reported on the same line:
   copy          (leg "copy", off by default) a plain 1 GiB device copy, the
                 calibration kernel for the FETCH_SIZE / WRITE_SIZE counters
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+Every leg first runs its step untimed for --settle-s seconds (default 0.5)
+so that the GPU's clocks have ramped up under the load before the W warmup
+and K timed steps; without it the first few dozen calls of a leg run up to
+25 % slower and a short run times the ramp.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--settle-s S]
 """
 
 from __future__ import annotations
@@ -89,6 +94,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--legs", default="select,score,decode,backward,cpu",
                     help="comma list of: select, score, decode, backward, cpu, copy")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="untimed seconds of calls before each leg's warmup (clock ramp); 0 disables")
     ap.add_argument("--cpu-row-stride", type=int, default=2,
                     help="the CPU baseline runs every n-th row of the prefill workload")
     return ap.parse_args()
@@ -128,8 +135,20 @@ def visible_pairs(P, rows=None):
     return total
 
 
+SETTLE_S = 0.5
+
+
 def time_calls(fn, steps, warmup, torch):
-    """Runs fn warmup+steps times; returns (wall ms per step, mean event ms per call)."""
+    """Runs fn untimed for SETTLE_S seconds of wall time (the GPU raises its
+    clocks over the first tens of milliseconds under load, so a short warmup
+    would time the ramp instead of the steady state), then warmup more untimed
+    calls, then steps timed calls; returns (wall ms per step, mean event ms
+    per call)."""
+    t_end = time.perf_counter() + SETTLE_S
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn(0)
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
@@ -152,6 +171,8 @@ def main():
               "(the indexer shards by batch or rows with no communication, see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
     legs = set(args.legs.split(","))
+    global SETTLE_S
+    SETTLE_S = max(0.0, args.settle_s)
 
     import torch
 

@@ -35,29 +35,25 @@ namespace {
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kBwdWaves * kWave;
 
-// fp32 rounded to the nearest bf16 (ties to even), returned as the fp32 with
-// the same value.  Inputs are finite.
-__device__ __forceinline__ float bf16_round(float x)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bf16 (nearest, ties to even) and packed into one
+// dword, lo in bits 0-15, hi in 16-31: one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t cvt_pack_bf16(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(x);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return __uint_as_float(u & 0xFFFF0000u);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// Two bf16-valued floats packed into one dword: lo in bits 0-15, hi in 16-31.
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
-{
-    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// MFMA operand from eight bf16-valued floats (k index e = element e).
+// MFMA operand from eight floats rounded to bf16 (k index e = element e).
 __device__ __forceinline__ bf16x8 operand_from(const float (&v)[16], int base)
 {
     u32x4 u;
-    u.x = pack_bf16(v[base + 0], v[base + 1]);
-    u.y = pack_bf16(v[base + 2], v[base + 3]);
-    u.z = pack_bf16(v[base + 4], v[base + 5]);
-    u.w = pack_bf16(v[base + 6], v[base + 7]);
+    u.x = cvt_pack_bf16(v[base + 0], v[base + 1]);
+    u.y = cvt_pack_bf16(v[base + 2], v[base + 3]);
+    u.z = cvt_pack_bf16(v[base + 4], v[base + 5]);
+    u.w = cvt_pack_bf16(v[base + 6], v[base + 7]);
     return __builtin_bit_cast(bf16x8, u);
 }
 
@@ -187,7 +183,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         if (active && 32 * t < thr) {
             const uint16_t *T = tile[t & 1];
             // upstream gradient of this lane's 16 entries (0 where masked)
-            float ge[16], gb[16];
+            float ge[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int j = 32 * t + c_row(r, gi);
@@ -197,7 +193,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     ok = ok && a.k_seg[(int64_t)b * a.W + jc] == qseg;
                 const float gv = grow[jc];
                 ge[r] = ok ? gv : 0.0f;
-                gb[r] = bf16_round(ge[r]);
             }
             // transposed logits: lane = head n of this block, register r = entry c_row(r, gi)
             f32x16 lt;
@@ -212,7 +207,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             for (int r = 0; r < 16; ++r) {
                 const float x = lt[r];
                 dw_acc = fmaf(ge[r], relu(x), dw_acc);
-                pf[r] = x > 0.0f ? gb[r] : 0.0f;
+                pf[r] = x > 0.0f ? ge[r] : 0.0f; // rounded to bf16 by operand_from
             }
             const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
 #pragma unroll
@@ -396,7 +391,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const int r = 4 * q4 + c;
-                        pf[r] = lg[r] > 0.0f ? bf16_round(ge * wr[c]) : 0.0f;
+                        pf[r] = lg[r] > 0.0f ? ge * wr[c] : 0.0f; // rounded to bf16 by operand_from
                     }
                 }
                 const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
