@@ -89,9 +89,16 @@ __device__ __forceinline__ bool chunk_live(const BwdArgs &a, int b, int c, int j
 template <int D>
 struct RowTileGeom {
     static constexpr int kPitch = D + 8;                  // LDS row pitch (elements)
+    static constexpr int kPitchT = 32 + 8;                // transposed tile: entries per column + pad
     static constexpr int kChunks = 32 * D / 8;            // 16-byte pieces per 32-entry tile
     static constexpr int kPerThread = (kChunks + kBwdThreads - 1) / kBwdThreads;
 };
+
+// Position of entry e (0..31) of a key tile in a column of the transposed
+// tile: bits 2 and 3 swapped, so the eight entries 16jb + c_row(0..7, g) that
+// one lane contracts in the dq product sit at 16jb + 8g + 0..7, one 16-byte
+// read.
+__device__ __forceinline__ int tposed(int e) { return (e & 0x13) | ((e & 4) << 1) | ((e & 8) >> 1); }
 
 template <int D, int HB>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_rows_kernel(const BwdArgs a)
@@ -99,7 +106,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     using G = RowTileGeom<D>;
     constexpr int KS = D / 16, DB = D / 32, P = G::kPitch;
     constexpr int RPW = kBwdWaves / HB; // query rows per workgroup
+    constexpr int PT = G::kPitchT;
+    // key tile, entry-major (logits) and column-major (dq product)
     __shared__ __attribute__((aligned(16))) uint16_t tile[2][32 * P];
+    __shared__ __attribute__((aligned(16))) uint16_t tileT[2][D * PT];
+    // each row's upstream gradients of the tile, 0 where masked
+    __shared__ __attribute__((aligned(16))) float gtile[2][RPW][32];
 
     const int tid = threadIdx.x;
     const int wv = uniform(tid / kWave);
@@ -134,15 +146,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const float *grow = a.g + ((int64_t)b * a.S + (active ? i : 0)) * a.W;
     const uint16_t *kb = a.k + (int64_t)b * a.k_sb;
 
-    // LDS offsets of this lane's transposed key reads: entry 16jb + c_row(e, gi),
-    // column 32c + n.
-    int koff[2][8];
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            koff[jb][e] = (16 * jb + c_row(e, gi)) * P + n;
-
     f32x16 acc[DB];
 #pragma unroll
     for (int c = 0; c < DB; ++c)
@@ -150,12 +153,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             acc[c][r] = 0.0f;
     float dw_acc = 0.0f;
 
+    // Staging: piece c holds eight columns 8(c / 32) .. +7 of entry c % 32,
+    // so the lanes of a wave cover consecutive entries and their column-major
+    // stores fall in consecutive positions.
     uint4 pre[G::kPerThread];
     auto fetch = [&](int t) {
 #pragma unroll
         for (int u = 0; u < G::kPerThread; ++u) {
             const int c = tid + u * kBwdThreads;
-            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+            const int row = c % 32, col = (c / 32) * 8;
             const int j = 32 * t + row;
             pre[u] = make_uint4(0, 0, 0, 0);
             if (c < G::kChunks && j < a.W)
@@ -166,33 +172,66 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
         for (int u = 0; u < G::kPerThread; ++u) {
             const int c = tid + u * kBwdThreads;
-            const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-            if (c < G::kChunks)
+            const int row = c % 32, col = (c / 32) * 8;
+            if (c < G::kChunks) {
                 *reinterpret_cast<uint4 *>(&tile[buf][row * P + col]) = pre[u];
+                uint16_t *dst = &tileT[buf][col * PT + tposed(row)];
+                const uint32_t v[4] = {pre[u].x, pre[u].y, pre[u].z, pre[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dst[(2 * e) * PT] = (uint16_t)v[e];
+                    dst[(2 * e + 1) * PT] = (uint16_t)(v[e] >> 16);
+                }
+            }
         }
+    };
+
+    // The masked gradients of a row's tile are loaded once, by lanes 0..31 of
+    // the row's first head-block wave (one entry each), and staged in LDS
+    // with the key tile.
+    const int wr = wv / HB; // this wave's row within the workgroup
+    const bool g_lane = hb == 0 && l < 32;
+    float gnext = 0.0f;
+    auto fetch_g = [&](int t) {
+        if (g_lane && active) {
+            const int j = 32 * t + l;
+            const int jc = min(j, a.W - 1);
+            bool ok = j < thr;
+            if (a.k_seg)
+                ok = ok && a.k_seg[(int64_t)b * a.W + jc] == qseg;
+            const float gv = grow[jc];
+            gnext = ok ? gv : 0.0f;
+        }
+    };
+    auto store_g = [&](int buf) {
+        if (g_lane)
+            gtile[buf][wr][l] = gnext;
     };
 
     if (ntiles > 0) {
         fetch(0);
+        fetch_g(0);
         store(0);
+        store_g(0);
     }
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles)
+        if (t + 1 < ntiles) {
             fetch(t + 1);
+            fetch_g(t + 1);
+        }
         if (active && 32 * t < thr) {
             const uint16_t *T = tile[t & 1];
-            // upstream gradient of this lane's 16 entries (0 where masked)
+            // upstream gradient of this lane's 16 entries c_row(r, gi)
             float ge[16];
+            const float *gt = gtile[t & 1][wr];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int j = 32 * t + c_row(r, gi);
-                const int jc = min(j, a.W - 1);
-                bool ok = j < thr;
-                if (a.k_seg)
-                    ok = ok && a.k_seg[(int64_t)b * a.W + jc] == qseg;
-                const float gv = grow[jc];
-                ge[r] = ok ? gv : 0.0f;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 v = *reinterpret_cast<const float4 *>(gt + 8 * q4 + 4 * gi);
+                ge[4 * q4 + 0] = v.x;
+                ge[4 * q4 + 1] = v.y;
+                ge[4 * q4 + 2] = v.z;
+                ge[4 * q4 + 3] = v.w;
             }
             // transposed logits: lane = head n of this block, register r = entry c_row(r, gi)
             f32x16 lt;
@@ -210,14 +249,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 pf[r] = x > 0.0f ? ge[r] : 0.0f; // rounded to bf16 by operand_from
             }
             const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
+            const uint16_t *TT = tileT[t & 1] + n * PT + 8 * gi;
 #pragma unroll
             for (int c = 0; c < DB; ++c) {
-                acc[c] = mfma32(a0, gather8(T + 32 * c, koff[0]), acc[c]);
-                acc[c] = mfma32(a1, gather8(T + 32 * c, koff[1]), acc[c]);
+                acc[c] = mfma32(a0, load_frag(TT + 32 * c * PT), acc[c]);
+                acc[c] = mfma32(a1, load_frag(TT + 32 * c * PT + 16), acc[c]);
             }
         }
-        if (t + 1 < ntiles)
+        if (t + 1 < ntiles) {
             store((t + 1) & 1);
+            store_g((t + 1) & 1);
+        }
         __syncthreads();
     }
 
