@@ -392,7 +392,9 @@ csa_status csa_index_select(const csa_index_problem *p, const void *q, const voi
                 e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
             if (e != hipSuccess)
                 return fail(CSA_ERR_DEVICE, "cannot query the compute unit count");
-            if (!scores && c.rows <= csa::kStreamRows)
+            // the balanced kernel's tile prefix is 32-bit
+            const int64_t tiles_bound = c.rows * (((int64_t)p->W + csa::kTileEntries - 1) / csa::kTileEntries);
+            if (!scores && c.rows <= csa::kStreamRows && tiles_bound < 0x7FFFFFFF)
                 e = csa::launch_stream(p->D, c.HB, a, cus * csa::kStreamBlocksPerCU, s);
             else
                 e = csa::launch_split(p->D, c.HB, a, s);
