@@ -338,6 +338,13 @@ def test_sequence_major_q_and_padded_k_rows():
     i2, s2 = gpu_select(P, dev=d2, return_scores=True)
     np.testing.assert_array_equal(to_np(i2), to_np(ref_i))
     assert np.array_equal(to_np(s2).view(np.uint32), to_np(ref_s).view(np.uint32))
+    # every kernel takes the strides: row tiles, and the split plan's
+    # chunked (with scores) and balanced (selection only) kernels
+    for plan in ("row_tiles", "split_rows"):
+        np.testing.assert_array_equal(to_np(gpu_select(P, dev=d2, plan=plan)), to_np(ref_i))
+        i3, s3 = gpu_select(P, dev=d2, plan=plan, return_scores=True)
+        np.testing.assert_array_equal(to_np(i3), to_np(ref_i))
+        assert np.array_equal(to_np(s3).view(np.uint32), to_np(ref_s).view(np.uint32))
 
 
 BALANCED = [
