@@ -86,11 +86,15 @@ __device__ __forceinline__ bool chunk_live(const BwdArgs &a, int b, int c, int j
 // ---------------------------------------------------------------------------
 // Pass 1: dq and dw.
 
+// Entries per key tile of the row pass: two 32-entry subtiles between
+// barriers.
+constexpr int kRowTile = 64;
+
 template <int D>
 struct RowTileGeom {
     static constexpr int kPitch = D + 8;                  // LDS row pitch (elements)
-    static constexpr int kPitchT = 32 + 8;                // transposed tile: entries per column + pad
-    static constexpr int kChunks = 32 * D / 8;            // 16-byte pieces per 32-entry tile
+    static constexpr int kPitchT = kRowTile + 8;          // transposed tile: entries per column + pad
+    static constexpr int kChunks = kRowTile * D / 8;      // 16-byte pieces per key tile
     static constexpr int kPerThread = (kChunks + kBwdThreads - 1) / kBwdThreads;
 };
 
@@ -108,10 +112,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     constexpr int RPW = kBwdWaves / HB; // query rows per workgroup
     constexpr int PT = G::kPitchT;
     // key tile, entry-major (logits) and column-major (dq product)
-    __shared__ __attribute__((aligned(16))) uint16_t tile[2][32 * P];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[2][kRowTile * P];
     __shared__ __attribute__((aligned(16))) uint16_t tileT[2][D * PT];
     // each row's upstream gradients of the tile, 0 where masked
-    __shared__ __attribute__((aligned(16))) float gtile[2][RPW][32];
+    __shared__ __attribute__((aligned(16))) float gtile[2][RPW][kRowTile];
 
     const int tid = threadIdx.x;
     const int wv = uniform(tid / kWave);
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const bool active = i < a.S;
     const int64_t off = row_offset(a, b);
     const int last = min(i0 + RPW, a.S) - 1;
-    const int ntiles = (visible_entries(off + last, a.m, a.W) + 31) / 32;
+    const int ntiles = (visible_entries(off + last, a.m, a.W) + kRowTile - 1) / kRowTile;
     const int thr = active ? visible_entries(off + i, a.m, a.W) : 0;
     const int qseg = (active && a.q_seg) ? a.q_seg[(int64_t)b * a.S + i] : 0;
 
@@ -153,16 +157,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             acc[c][r] = 0.0f;
     float dw_acc = 0.0f;
 
-    // Staging: piece c holds eight columns 8(c / 32) .. +7 of entry c % 32,
-    // so the lanes of a wave cover consecutive entries and their column-major
-    // stores fall in consecutive positions.
+    // Staging: piece c holds eight columns 8(c / kRowTile) .. +7 of entry
+    // c % kRowTile, so the lanes of a wave cover consecutive entries and their
+    // column-major stores fall in consecutive positions.  In the column-major
+    // copy, subtile h of the tile occupies positions 32h .. 32h+31.
     uint4 pre[G::kPerThread];
     auto fetch = [&](int t) {
 #pragma unroll
         for (int u = 0; u < G::kPerThread; ++u) {
             const int c = tid + u * kBwdThreads;
-            const int row = c % 32, col = (c / 32) * 8;
-            const int j = 32 * t + row;
+            const int row = c % kRowTile, col = (c / kRowTile) * 8;
+            const int j = kRowTile * t + row;
             pre[u] = make_uint4(0, 0, 0, 0);
             if (c < G::kChunks && j < a.W)
                 pre[u] = *reinterpret_cast<const uint4 *>(kb + (int64_t)j * a.k_sw + col);
@@ -172,10 +177,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
         for (int u = 0; u < G::kPerThread; ++u) {
             const int c = tid + u * kBwdThreads;
-            const int row = c % 32, col = (c / 32) * 8;
+            const int row = c % kRowTile, col = (c / kRowTile) * 8;
             if (c < G::kChunks) {
                 *reinterpret_cast<uint4 *>(&tile[buf][row * P + col]) = pre[u];
-                uint16_t *dst = &tileT[buf][col * PT + tposed(row)];
+                uint16_t *dst = &tileT[buf][col * PT + (row & ~31) + tposed(row & 31)];
                 const uint32_t v[4] = {pre[u].x, pre[u].y, pre[u].z, pre[u].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -186,15 +191,16 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         }
     };
 
-    // The masked gradients of a row's tile are loaded once, by lanes 0..31 of
-    // the row's first head-block wave (one entry each), and staged in LDS
-    // with the key tile.
+    // The masked gradients of a row's tile are loaded once, by the row's
+    // first head-block wave (one entry per lane), and staged in LDS with the
+    // key tile.
+    static_assert(kRowTile == kWave, "one gradient per lane");
     const int wr = wv / HB; // this wave's row within the workgroup
-    const bool g_lane = hb == 0 && l < 32;
+    const bool g_lane = hb == 0;
     float gnext = 0.0f;
     auto fetch_g = [&](int t) {
         if (g_lane && active) {
-            const int j = 32 * t + l;
+            const int j = kRowTile * t + l;
             const int jc = min(j, a.W - 1);
             bool ok = j < thr;
             if (a.k_seg)
@@ -220,11 +226,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             fetch(t + 1);
             fetch_g(t + 1);
         }
-        if (active && 32 * t < thr) {
-            const uint16_t *T = tile[t & 1];
+#pragma unroll
+        for (int hs = 0; hs < kRowTile / 32; ++hs) {
+        if (active && kRowTile * t + 32 * hs < thr) {
+            const uint16_t *T = tile[t & 1] + 32 * hs * P;
             // upstream gradient of this lane's 16 entries c_row(r, gi)
             float ge[16];
-            const float *gt = gtile[t & 1][wr];
+            const float *gt = gtile[t & 1][wr] + 32 * hs;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const float4 v = *reinterpret_cast<const float4 *>(gt + 8 * q4 + 4 * gi);
@@ -249,12 +257,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 pf[r] = x > 0.0f ? ge[r] : 0.0f; // rounded to bf16 by operand_from
             }
             const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
-            const uint16_t *TT = tileT[t & 1] + n * PT + 8 * gi;
+            const uint16_t *TT = tileT[t & 1] + n * PT + 32 * hs + 8 * gi;
 #pragma unroll
             for (int c = 0; c < DB; ++c) {
                 acc[c] = mfma32(a0, load_frag(TT + 32 * c * PT), acc[c]);
                 acc[c] = mfma32(a1, load_frag(TT + 32 * c * PT + 16), acc[c]);
             }
+        }
         }
         if (t + 1 < ntiles) {
             store((t + 1) & 1);
