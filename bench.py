@@ -167,8 +167,8 @@ def time_calls(fn, steps, warmup, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the indexer shards by batch or rows with no communication, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the indexer would shard by batch or by rows with no communication between GPUs)", file=sys.stderr)
         sys.exit(2)
     legs = set(args.legs.split(","))
     global SETTLE_S
