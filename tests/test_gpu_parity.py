@@ -151,7 +151,8 @@ def test_topk_long_rows_exact(dist):
     s[2, 100:] = -np.inf          # fewer valid entries than k
     s[3, :] = 0.0                 # all ties
     s[3, ::7] = -0.0
-    for k in (1, 512, 2048):
+    # k not a multiple of 64 as well
+    for k in (1, 100, 300, 512, 2048):
         np.testing.assert_array_equal(to_np(csa.topk(torch.from_numpy(s).cuda(), k)), oracle.topk(s, k),
                                       err_msg=f"{dist} k={k}")
     # a row length that is not a multiple of 4 or of 64
