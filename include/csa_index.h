@@ -75,7 +75,9 @@ typedef enum csa_plan {
  *   w : [B,S,H] bf16 at w + b*w_sb + i*w_ss + h
  * Supported: D in {32, 64, 128}; 1 <= H <= 128; q and k 16-byte aligned with
  * strides that are multiples of 8 elements; k_sw < 2^24; W <= 2^30; m >= 1;
- * finite scale.
+ * finite scale.  Strides may be smaller than the row they step over: k_sw < D
+ * makes entries overlap and k_sw = 0 repeats one entry (the kernels read the
+ * D values at each entry's own address, whatever the stride).
  */
 typedef struct csa_index_problem {
     int32_t B, S, H, D, W;

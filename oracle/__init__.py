@@ -12,6 +12,7 @@ and return numpy arrays.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 from typing import Optional, Sequence
@@ -149,14 +150,15 @@ def select(P, rows: Optional[Sequence[int]] = None):
     return s, topk(s, P.top_k)
 
 
-def backward(P, g: np.ndarray, bounds: bool = False):
+def backward(P, g: np.ndarray, stats: bool = False):
     """Gradients of sum(g * score) over unmasked (i, j), float64.
 
     g is the upstream gradient of the scores, [B, S, W] float32 (its values at
     masked positions are ignored).  Returns (dq [B,H,S,D], dk [B,W,D],
-    dw [B,S,H]); with bounds=True also (bq, bk, bw): per-element bounds on the
-    distance of a float32 implementation that rounds the gradient operand to
-    bf16 once (see csa_oracle.c).
+    dw [B,S,H]); with stats=True also (sq, sk, sw), the same shapes with a
+    last axis of 3 per element: the sum of |term| and of term^2 over the
+    terms whose ReLU derivative is decided, and the undecided mass (see
+    csa_oracle.c).  error_bounds() turns them into bounds.
     """
     _check(P)
     gg = np.ascontiguousarray(g, dtype=np.float32)
@@ -168,19 +170,19 @@ def backward(P, g: np.ndarray, bounds: bool = False):
     dq = np.empty((P.B, P.H, P.S, P.D), np.float64)
     dk = np.empty((P.B, P.W, P.D), np.float64)
     dw = np.empty((P.B, P.S, P.H), np.float64)
-    bq = np.empty_like(dq) if bounds else None
-    bk = np.empty_like(dk) if bounds else None
-    bw = np.empty_like(dw) if bounds else None
+    sq = np.empty(dq.shape + (3,)) if stats else None
+    sk = np.empty(dk.shape + (3,)) if stats else None
+    sw = np.empty(dw.shape + (3,)) if stats else None
     lib.csa_oracle_backward_f64(P.B, P.S, P.H, P.D, P.W, P.m, float(P.scale), _ptr(q), _ptr(k), _ptr(w),
                                 _ptr(qo), _ptr(qs), _ptr(ks), _ptr(gg), _ptr(dq), _ptr(dk), _ptr(dw),
-                                _ptr(bq), _ptr(bk), _ptr(bw))
-    return (dq, dk, dw, bq, bk, bw) if bounds else (dq, dk, dw)
+                                _ptr(sq), _ptr(sk), _ptr(sw))
+    return (dq, dk, dw, sq, sk, sw) if stats else (dq, dk, dw)
 
 
 def backward_sample(P, g: np.ndarray, rows: Sequence[int], entries: Sequence[int]):
     """The gradients of backward() for chosen rows (b*S+i) and entries (b*W+j):
-    (dq [n_rows,H,D], dw [n_rows,H], dk [n_entries,D], bq, bw, bk), float64,
-    with the same bounds."""
+    (dq [n_rows,H,D], dw [n_rows,H], dk [n_entries,D], sq, sw, sk), float64,
+    with the same per-element statistics (last axis 3)."""
     _check(P)
     gg = np.ascontiguousarray(g, dtype=np.float32)
     if gg.shape != (P.B, P.S, P.W):
@@ -197,8 +199,54 @@ def backward_sample(P, g: np.ndarray, rows: Sequence[int], entries: Sequence[int
     dq = np.empty((r.size, P.H, P.D), np.float64)
     dw = np.empty((r.size, P.H), np.float64)
     dk = np.empty((e.size, P.D), np.float64)
-    bq, bw, bk = np.empty_like(dq), np.empty_like(dw), np.empty_like(dk)
+    sq, sw, sk = np.empty(dq.shape + (3,)), np.empty(dw.shape + (3,)), np.empty(dk.shape + (3,))
     lib.csa_oracle_backward_sample_f64(P.B, P.S, P.H, P.D, P.W, P.m, float(P.scale), _ptr(q), _ptr(k), _ptr(w),
                                        _ptr(qo), _ptr(qs), _ptr(ks), _ptr(gg), r.size, _ptr(r), e.size, _ptr(e),
-                                       _ptr(dq), _ptr(dw), _ptr(dk), _ptr(bq), _ptr(bw), _ptr(bk))
-    return dq, dw, dk, bq, bw, bk
+                                       _ptr(dq), _ptr(dw), _ptr(dk), _ptr(sq), _ptr(sw), _ptr(sk))
+    return dq, dw, dk, sq, sw, sk
+
+
+# Unit roundoffs of float32 and bfloat16 (round to nearest).
+U_F32 = 2.0 ** -24
+U_BF16 = 2.0 ** -9
+# Confidence parameter of the bounds (the same value the C oracle uses for
+# its logit bound eps_l).
+LAMBDA = 8.0
+
+
+def sum_bound_factor(n: int) -> float:
+    """exp(LAMBDA sqrt(n) u + n u^2 / (1 - u)) - 1: a float32 sum of n terms
+    lies within this factor times sum|x| of the exact sum with probability at
+    least 1 - 2 n exp(-LAMBDA^2 (1 - u)^2 / 2) (Higham and Mary 2019, the
+    probabilistic rounding error analysis of summation and inner products)."""
+    return math.expm1(LAMBDA * math.sqrt(n) * U_F32 + n * U_F32 * U_F32 / (1.0 - U_F32))
+
+
+def error_bounds(value: np.ndarray, stats: np.ndarray, n: int, bf16_operand: bool) -> np.ndarray:
+    """Per-element bound on |fp32 result - oracle float64 value| of one gradient.
+
+    value: the oracle's float64 gradient; stats: its statistics (last axis:
+    sum |t| and sum t^2 over the terms whose ReLU derivative is decided, and
+    the undecided mass U); n: the longest chain of float32 additions an
+    implementation accumulates for one element; bf16_operand: whether each
+    term's gradient operand (g [l>0] for dq, g w [l>0] for dk) is rounded to
+    bfloat16 once (round to nearest) before the product.
+
+    bound = U + LAMBDA (u_bf16 + 2u) sqrt(sum t^2) [bf16 operand only]
+              + sum_bound_factor(n) sum|t| + 4 u |value|
+
+    The rounding errors of the bf16 operands are independent, bounded by
+    u_bf16 (plus u for an fp32 product rounded first) and of mean zero, so
+    their weighted sum exceeds LAMBDA (u_bf16 + 2u) sqrt(sum t^2) with
+    probability below 2 exp(-LAMBDA^2 / 2) (Hoeffding's inequality).  The
+    float32 accumulation is covered by the summation bound, the final
+    multiplies (scale, weight) by 4u |value|.  U counts in full every term
+    whose fp32 logit may have the other sign (for dw: the most that fp32
+    logits can move ReLU(l)).  Each part fails with probability below 1e-9
+    per element at the sizes used.
+    """
+    a, r2, und = stats[..., 0], stats[..., 1], stats[..., 2]
+    b = und + sum_bound_factor(n) * a + 4 * U_F32 * np.abs(value)
+    if bf16_operand:
+        b = b + LAMBDA * (U_BF16 + 2 * U_F32) * np.sqrt(r2)
+    return b

@@ -211,8 +211,20 @@ void csa_oracle_topk(int64_t rows, int64_t W, int64_t top_k, const float *scores
     }
 }
 
-/* One logit in float64, its sum of absolute products, and the float32 error
- * bound eps_l on it (see csa_oracle_backward_f64). */
+/* Probabilistic bound factor of float32 summation of n terms (Higham and
+ * Mary 2019): the computed sum lies within
+ * (exp(lambda sqrt(n) u + n u^2 / (1-u)) - 1) sum|x| of the exact one with
+ * probability at least 1 - 2 n exp(-lambda^2 (1-u)^2 / 2), u = 2^-24.  With
+ * lambda = 8 and n <= 2^14 that is 1 - 4e-10. */
+static double sum_bound_factor(int64_t n)
+{
+    const double u = ldexp(1.0, -24), lambda = 8.0;
+    return expm1(lambda * sqrt((double)n) * u + (double)n * u * u / (1.0 - u));
+}
+
+/* One logit in float64, and eps_l, the bound above on how far a float32 dot
+ * product of the same bf16 values (products exact, n = D additions) may lie
+ * from it. */
 static double logit_f64(const uint16_t *qr, const uint16_t *kr, int64_t D, double *eps_l)
 {
     double logit = 0.0, mag = 0.0;
@@ -221,7 +233,7 @@ static double logit_f64(const uint16_t *qr, const uint16_t *kr, int64_t D, doubl
         logit = logit + prod;
         mag = mag + fabs(prod);
     }
-    *eps_l = 2.0 * (double)(D + 8) * ldexp(1.0, -24) * mag;
+    *eps_l = sum_bound_factor(D) * mag;
     return logit;
 }
 
@@ -240,35 +252,35 @@ static double logit_f64(const uint16_t *qr, const uint16_t *kr, int64_t D, doubl
  * ReLU's derivative at 0 is taken as 0, matching ReLU(l) = (l > 0 ? l : 0).
  * Everything is accumulated in float64 in the order written.
  *
- * When the bound arrays are non-NULL the same loops also produce, per output
- * element, a bound on how far a float32 implementation may lie from the
- * float64 value:
- *   - each logit computed in float32 is within eps_l = 2 (D+8) 2^-24
- *     sum_t |q_t k_t| of l, so a term whose |l| <= eps_l has an undecided
- *     [l > 0]: its full magnitude goes into the bound of dq and dk, and
- *     |g| eps_l into the bound of dw;
- *   - every other term may be off by rel = 2 (2^-9 + (n + 8) 2^-24) of its
- *     magnitude, n the longest sum: the gradient operand rounded to bf16 once
- *     (2^-9) plus float32 accumulation.
- * dq/bq are [B,H,S,D], dk/bk [B,W,D], dw/bw [B,S,H]; g is [B,S,W] float32.
- * The three bound arrays are all NULL or all set.
+ * When the statistics arrays are non-NULL the same loops also record, per
+ * output element, three sums over the element's terms from which a caller
+ * bounds how far a float32 implementation may lie from the float64 value
+ * (the terms are the summands above, e.g. scale g w k_t for dq):
+ *   [0] sum of |term| over the terms whose [l > 0] is decided,
+ *   [1] sum of term^2 over the same terms,
+ *   [2] for dq and dk the sum of |term| over the undecided terms, those whose
+ *       |l| <= eps_l, so that a float32 logit may have either sign; for dw
+ *       the sum over all terms of |scale g| eps_l, the most that float32
+ *       logits can move ReLU(l) by.
+ * dq/sq are [B,H,S,D] (sq with 3 doubles per element), dk/sk [B,W,D],
+ * dw/sw [B,S,H]; g is [B,S,W] float32.  sq, sk and sw are all NULL or all set.
  */
-/* dq [H][D] and dw [H] of query row (b, i), with bounds when bq != NULL. */
+/* dq [H][D] and dw [H] of query row (b, i), with statistics when sq != NULL. */
 static void backward_row(int64_t b, int64_t i, int64_t S, int64_t H, int64_t D, int64_t W, int64_t m,
-                         double scale, double rel, const uint16_t *q, const uint16_t *k, const uint16_t *w,
+                         double scale, const uint16_t *q, const uint16_t *k, const uint16_t *w,
                          const int32_t *q_offset, const int32_t *q_seg, const int32_t *k_seg, const float *g,
-                         double *dq, double *dw, double *bq, double *bw)
+                         double *dq, double *dw, double *sq, double *sw)
 {
     for (int64_t h = 0; h < H; ++h) {
         const uint16_t *qr = &q[((b * H + h) * S + i) * D];
         double wv = (double)bf16_value(w[(b * S + i) * H + h]);
         double *dqr = &dq[h * D];
-        double *bqr = bq ? &bq[h * D] : NULL;
-        double dwv = 0.0, bwv = 0.0;
+        double *sqr = sq ? &sq[h * D * 3] : NULL;
+        double dwv = 0.0, sw_abs = 0.0, sw_sq = 0.0, sw_lg = 0.0;
         for (int64_t t = 0; t < D; ++t) {
             dqr[t] = 0.0;
-            if (bqr)
-                bqr[t] = 0.0;
+            if (sqr)
+                sqr[3 * t] = sqr[3 * t + 1] = sqr[3 * t + 2] = 0.0;
         }
         for (int64_t j = 0; j < W; ++j) {
             if (!entry_is_valid(b, i, j, S, W, m, q_offset, q_seg, k_seg))
@@ -278,35 +290,47 @@ static void backward_row(int64_t b, int64_t i, int64_t S, int64_t H, int64_t D, 
             double eps_l;
             double logit = logit_f64(qr, kr, D, &eps_l);
             double relu = logit > 0.0 ? logit : 0.0;
-            dwv += scale * gv * relu;
-            bwv += fabs(scale) * fabs(gv) * (eps_l + rel * relu);
+            double tw = scale * gv * relu;
+            dwv += tw;
+            sw_abs += fabs(tw);
+            sw_sq += tw * tw;
+            sw_lg += fabs(scale * gv) * eps_l;
             int undecided = fabs(logit) <= eps_l;
             double c = scale * gv * wv;
             for (int64_t t = 0; t < D; ++t) {
-                double kv = (double)bf16_value(kr[t]);
+                double term = c * (double)bf16_value(kr[t]);
                 if (logit > 0.0)
-                    dqr[t] += c * kv;
-                if (bqr)
-                    bqr[t] += (undecided ? 1.0 : rel) * fabs(c * kv);
+                    dqr[t] += term;
+                if (sqr) {
+                    if (undecided) {
+                        sqr[3 * t + 2] += fabs(term);
+                    } else if (logit > 0.0) {
+                        sqr[3 * t] += fabs(term);
+                        sqr[3 * t + 1] += term * term;
+                    }
+                }
             }
         }
         dw[h] = dwv;
-        if (bw)
-            bw[h] = bwv;
+        if (sw) {
+            sw[3 * h] = sw_abs;
+            sw[3 * h + 1] = sw_sq;
+            sw[3 * h + 2] = sw_lg;
+        }
     }
 }
 
 /* dk [D] of entry (b, j): rows i in order, heads h in order. */
 static void backward_entry(int64_t b, int64_t j, int64_t S, int64_t H, int64_t D, int64_t W, int64_t m,
-                           double scale, double rel, const uint16_t *q, const uint16_t *k, const uint16_t *w,
+                           double scale, const uint16_t *q, const uint16_t *k, const uint16_t *w,
                            const int32_t *q_offset, const int32_t *q_seg, const int32_t *k_seg, const float *g,
-                           double *dk, double *bk)
+                           double *dk, double *sk)
 {
     const uint16_t *kr = &k[(b * W + j) * D];
     for (int64_t t = 0; t < D; ++t) {
         dk[t] = 0.0;
-        if (bk)
-            bk[t] = 0.0;
+        if (sk)
+            sk[3 * t] = sk[3 * t + 1] = sk[3 * t + 2] = 0.0;
     }
     for (int64_t i = 0; i < S; ++i) {
         if (!entry_is_valid(b, i, j, S, W, m, q_offset, q_seg, k_seg))
@@ -317,83 +341,86 @@ static void backward_entry(int64_t b, int64_t j, int64_t S, int64_t H, int64_t D
             double eps_l;
             double logit = logit_f64(qr, kr, D, &eps_l);
             int undecided = fabs(logit) <= eps_l;
-            if (!(logit > 0.0) && !(bk && undecided))
+            if (!(logit > 0.0) && !(sk && undecided))
                 continue;
             double c = scale * gv * (double)bf16_value(w[(b * S + i) * H + h]);
             for (int64_t t = 0; t < D; ++t) {
-                double qv = (double)bf16_value(qr[t]);
+                double term = c * (double)bf16_value(qr[t]);
                 if (logit > 0.0)
-                    dk[t] += c * qv;
-                if (bk)
-                    bk[t] += (undecided ? 1.0 : rel) * fabs(c * qv);
+                    dk[t] += term;
+                if (sk) {
+                    if (undecided) {
+                        sk[3 * t + 2] += fabs(term);
+                    } else {
+                        sk[3 * t] += fabs(term);
+                        sk[3 * t + 1] += term * term;
+                    }
+                }
             }
         }
     }
-}
-
-static double backward_rel(int64_t S, int64_t H, int64_t W)
-{
-    int64_t n_max = S * H > W ? S * H : W;
-    return 2.0 * (ldexp(1.0, -9) + (double)(n_max + 8) * ldexp(1.0, -24));
 }
 
 void csa_oracle_backward_f64(int64_t B, int64_t S, int64_t H, int64_t D, int64_t W, int64_t m,
                              double scale, const uint16_t *q, const uint16_t *k, const uint16_t *w,
                              const int32_t *q_offset, const int32_t *q_seg, const int32_t *k_seg,
                              const float *g, double *dq, double *dk, double *dw,
-                             double *bq, double *bk, double *bw)
+                             double *sq, double *sk, double *sw)
 {
-    double rel = backward_rel(S, H, W);
 #pragma omp parallel
     {
         double *rq = (double *)malloc(sizeof(double) * (size_t)(H * D));
-        double *rb = (double *)malloc(sizeof(double) * (size_t)(H * D));
+        double *rs = (double *)malloc(sizeof(double) * (size_t)(H * D * 3));
 #pragma omp for schedule(dynamic, 1)
         for (int64_t row = 0; row < B * S; ++row) {
             int64_t b = row / S, i = row % S;
-            backward_row(b, i, S, H, D, W, m, scale, rel, q, k, w, q_offset, q_seg, k_seg, g, rq,
-                         &dw[row * H], bq ? rb : NULL, bw ? &bw[row * H] : NULL);
+            backward_row(b, i, S, H, D, W, m, scale, q, k, w, q_offset, q_seg, k_seg, g, rq, &dw[row * H],
+                         sq ? rs : NULL, sw ? &sw[row * H * 3] : NULL);
             for (int64_t h = 0; h < H; ++h)
                 for (int64_t t = 0; t < D; ++t) {
-                    dq[((b * H + h) * S + i) * D + t] = rq[h * D + t];
-                    if (bq)
-                        bq[((b * H + h) * S + i) * D + t] = rb[h * D + t];
+                    int64_t o = ((b * H + h) * S + i) * D + t;
+                    dq[o] = rq[h * D + t];
+                    if (sq) {
+                        sq[3 * o] = rs[3 * (h * D + t)];
+                        sq[3 * o + 1] = rs[3 * (h * D + t) + 1];
+                        sq[3 * o + 2] = rs[3 * (h * D + t) + 2];
+                    }
                 }
         }
         free(rq);
-        free(rb);
+        free(rs);
     }
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t e = 0; e < B * W; ++e)
-        backward_entry(e / W, e % W, S, H, D, W, m, scale, rel, q, k, w, q_offset, q_seg, k_seg, g,
-                       &dk[e * D], bk ? &bk[e * D] : NULL);
+        backward_entry(e / W, e % W, S, H, D, W, m, scale, q, k, w, q_offset, q_seg, k_seg, g, &dk[e * D],
+                       sk ? &sk[e * D * 3] : NULL);
 }
 
 /*
  * The same gradients for chosen query rows and entries only: dq [n_rows,H,D]
  * and dw [n_rows,H] of rows[r] = b*S + i, dk [n_entries,D] of entries[e] =
- * b*W + j, with bounds as above (all bound arrays NULL or all set).
+ * b*W + j, with statistics as above (3 doubles per element; all NULL or all
+ * set).
  */
 void csa_oracle_backward_sample_f64(int64_t B, int64_t S, int64_t H, int64_t D, int64_t W, int64_t m,
                                     double scale, const uint16_t *q, const uint16_t *k, const uint16_t *w,
                                     const int32_t *q_offset, const int32_t *q_seg, const int32_t *k_seg,
                                     const float *g, int64_t n_rows, const int64_t *rows, int64_t n_entries,
-                                    const int64_t *entries, double *dq, double *dw, double *dk, double *bq,
-                                    double *bw, double *bk)
+                                    const int64_t *entries, double *dq, double *dw, double *dk, double *sq,
+                                    double *sw, double *sk)
 {
     (void)B;
-    double rel = backward_rel(S, H, W);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < n_rows; ++r)
-        backward_row(rows[r] / S, rows[r] % S, S, H, D, W, m, scale, rel, q, k, w, q_offset, q_seg, k_seg, g,
-                     &dq[r * H * D], &dw[r * H], bq ? &bq[r * H * D] : NULL, bw ? &bw[r * H] : NULL);
+        backward_row(rows[r] / S, rows[r] % S, S, H, D, W, m, scale, q, k, w, q_offset, q_seg, k_seg, g,
+                     &dq[r * H * D], &dw[r * H], sq ? &sq[r * H * D * 3] : NULL, sw ? &sw[r * H * 3] : NULL);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t e = 0; e < n_entries; ++e)
-        backward_entry(entries[e] / W, entries[e] % W, S, H, D, W, m, scale, rel, q, k, w, q_offset, q_seg,
-                       k_seg, g, &dk[e * D], bk ? &bk[e * D] : NULL);
+        backward_entry(entries[e] / W, entries[e] % W, S, H, D, W, m, scale, q, k, w, q_offset, q_seg, k_seg,
+                       g, &dk[e * D], sk ? &sk[e * D * 3] : NULL);
 }
 
-int csa_oracle_version(void) { return 1; }
+int csa_oracle_version(void) { return 2; }
 
 /* OpenMP threads the oracle's parallel loops use. */
 int csa_oracle_threads(void) { return omp_get_max_threads(); }

@@ -164,20 +164,31 @@ def _problem(q, k, w, compress_rate, scale, plan):
     return p
 
 
-def _masks(q, q_offset, q_seg, k_seg):
+def check_mask_shapes(B: int, S: int, W: int, q_offset=None, q_seg=None, k_seg=None) -> None:
+    """Shape, dtype and layout checks of the optional mask tensors (no device
+    access): q_offset [B], q_seg [B,S], k_seg [B,W], all contiguous int32, and
+    q_seg and k_seg both given or both omitted.  The kernels read every one of
+    these elements, so a short tensor is refused here, before any launch."""
+    for name, t, shape in (("q_offset", q_offset, (B,)), ("q_seg", q_seg, (B, S)), ("k_seg", k_seg, (B, W))):
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32:
+            raise ValueError(f"{name} must be an int32 tensor")
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {list(shape)} int32 tensor, got {tuple(t.shape)}")
+    if (q_seg is None) != (k_seg is None):
+        raise ValueError("q_seg and k_seg must be given together")
+
+
+def _masks(q, k, q_offset, q_seg, k_seg):
     B, _, S, _ = q.shape
-    if q_offset is not None:
-        _dev_tensor(q_offset, "q_offset", torch.int32, 1)
-        if q_offset.shape[0] != B or not q_offset.is_contiguous():
-            raise ValueError("q_offset must be a contiguous [B] int32 tensor")
-    if q_seg is not None:
-        _dev_tensor(q_seg, "q_seg", torch.int32, 2)
-        if tuple(q_seg.shape) != (B, S) or not q_seg.is_contiguous():
-            raise ValueError("q_seg must be a contiguous [B,S] int32 tensor")
-    if k_seg is not None:
-        _dev_tensor(k_seg, "k_seg", torch.int32, 2)
-        if k_seg.shape[0] != B or not k_seg.is_contiguous():
-            raise ValueError("k_seg must be a contiguous [B,W] int32 tensor")
+    W = k.shape[1]
+    for name, t in (("q_offset", q_offset), ("q_seg", q_seg), ("k_seg", k_seg)):
+        if t is not None:
+            _dev_tensor(t, name, torch.int32, t.dim())
+            if t.device != q.device:
+                raise ValueError(f"{name} must be on the device of q")
+    check_mask_shapes(B, S, W, q_offset, q_seg, k_seg)
     return _Masks(q_offset.data_ptr() if q_offset is not None else None,
                   q_seg.data_ptr() if q_seg is not None else None,
                   k_seg.data_ptr() if k_seg is not None else None)
@@ -208,7 +219,7 @@ def score(q, k, w, compress_rate: int, scale: float = 1.0, q_offset=None, q_seg=
     """Masked indexer scores [B,S,W] fp32 (csa_index_score)."""
     lib = load_library()
     p = _problem(q, k, w, compress_rate, scale, plan)
-    m = _masks(q, q_offset, q_seg, k_seg)
+    m = _masks(q, k, q_offset, q_seg, k_seg)
     if out is None:
         out = torch.empty((p.B, p.S, p.W), dtype=torch.float32, device=q.device)
     else:
@@ -248,7 +259,7 @@ def select(q, k, w, top_k: int, compress_rate: int, scale: float = 1.0, q_offset
     """Fused score + top-k (csa_index_select): idx [B,S,top_k] int32, and scores if asked."""
     lib = load_library()
     p = _problem(q, k, w, compress_rate, scale, plan)
-    m = _masks(q, q_offset, q_seg, k_seg)
+    m = _masks(q, k, q_offset, q_seg, k_seg)
     dev = q.device
     if out is None:
         out = torch.empty((p.B, p.S, int(top_k)), dtype=torch.int32, device=dev)
@@ -291,7 +302,7 @@ def score_backward(q, k, w, grad, compress_rate: int, scale: float = 1.0, q_offs
     over unmasked pairs (csa_index_score_backward); grad is [B,S,W] fp32."""
     lib = load_library()
     p = _problem(q, k, w, compress_rate, scale, "auto")
-    m = _masks(q, q_offset, q_seg, k_seg)
+    m = _masks(q, k, q_offset, q_seg, k_seg)
     dev = q.device
     _dev_tensor(grad, "grad", torch.float32, 3)
     if tuple(grad.shape) != (p.B, p.S, p.W) or not grad.is_contiguous():

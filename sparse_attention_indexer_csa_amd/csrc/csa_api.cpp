@@ -4,9 +4,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "csa_backward.hpp"
@@ -162,16 +164,65 @@ csa::KernelArgs make_args(const csa_index_problem *p, const Checked &c, const vo
     return a;
 }
 
-csa_status device_lds_limit(size_t need, const char *what)
+// Device properties the host code needs (LDS per workgroup, compute units),
+// queried once per device and kept for the life of the process.
+struct DeviceInfo {
+    int lds = 0;
+    int cus = 0;
+    hipError_t err = hipSuccess;
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_info_mutex;
+std::atomic<bool> g_info_ready[kMaxDevices];
+DeviceInfo g_info[kMaxDevices]; // written once, under the mutex, before its flag is set
+
+DeviceInfo query_device(int dev)
+{
+    DeviceInfo d;
+    d.err = hipDeviceGetAttribute(&d.lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (d.err == hipSuccess)
+        d.err = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return d;
+}
+
+// Properties of the calling thread's current device.
+csa_status current_device(DeviceInfo &out)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return fail(CSA_ERR_DEVICE, "hipGetDevice failed");
-    int lim = 0;
-    if (hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-        return fail(CSA_ERR_DEVICE, "cannot query the LDS limit");
-    if (need > (size_t)lim)
-        return fail(CSA_ERR_UNSUPPORTED, "%s needs %zu bytes of LDS per workgroup, device allows %d", what, need, lim);
+    if (dev < 0 || dev >= kMaxDevices) {
+        out = query_device(dev);
+    } else if (g_info_ready[dev].load(std::memory_order_acquire)) {
+        out = g_info[dev];
+    } else {
+        // only a successful query is kept; a failed one is retried next call
+        std::lock_guard<std::mutex> lock(g_info_mutex);
+        if (!g_info_ready[dev].load(std::memory_order_relaxed)) {
+            out = query_device(dev);
+            if (out.err == hipSuccess) {
+                g_info[dev] = out;
+                g_info_ready[dev].store(true, std::memory_order_release);
+            }
+        } else {
+            out = g_info[dev];
+        }
+    }
+    if (out.err != hipSuccess)
+        return fail(CSA_ERR_DEVICE, "cannot query device %d: %s", dev, hipGetErrorString(out.err));
+    return CSA_OK;
+}
+
+csa_status device_lds_limit(size_t need, const char *what)
+{
+    DeviceInfo d;
+    csa_status st = current_device(d);
+    if (st != CSA_OK)
+        return st;
+    if (need > (size_t)d.lds)
+        return fail(CSA_ERR_UNSUPPORTED, "%s needs %zu bytes of LDS per workgroup, device allows %d", what, need,
+                    d.lds);
     return CSA_OK;
 }
 
@@ -182,23 +233,15 @@ csa_status launched(hipError_t e, const char *what)
     return ok();
 }
 
-int device_lds(int *lim)
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return -1;
-    if (hipDeviceGetAttribute(lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-        return -1;
-    return 0;
-}
-
 // Top-k over rows of length up to W: the workgroup-per-row kernel for long
 // rows when its LDS fits, else one wave per row.
 csa_status launch_topk_rows(csa::KernelArgs &a, hipStream_t s)
 {
-    int lim = 0;
-    if (device_lds(&lim) != 0)
-        return fail(CSA_ERR_DEVICE, "cannot query the device's LDS limit");
+    DeviceInfo d;
+    csa_status st = current_device(d);
+    if (st != CSA_OK)
+        return st;
+    const int lim = d.lds;
     size_t block_lds = csa::topk_block_lds_bytes(a.cap, a.top_k);
     if (a.W >= csa::kTopkBlockMinLen && block_lds <= (size_t)lim)
         return launched(csa::launch_topk_block(a, block_lds, s), "top-k");
@@ -386,12 +429,11 @@ csa_status csa_index_select(const csa_index_problem *p, const void *q, const voi
         if (p->W > 0) {
             // without a score output only the visible prefixes are needed:
             // few rows take the balanced split, others the chunked one
-            int cus = 0, dev = 0;
-            hipError_t e = hipGetDevice(&dev);
-            if (e == hipSuccess)
-                e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-            if (e != hipSuccess)
-                return fail(CSA_ERR_DEVICE, "cannot query the compute unit count");
+            DeviceInfo dinfo;
+            if ((st = current_device(dinfo)) != CSA_OK)
+                return st;
+            const int cus = dinfo.cus;
+            hipError_t e;
             // the balanced kernel's tile prefix is 32-bit
             const int64_t tiles_bound = c.rows * (((int64_t)p->W + csa::kTileEntries - 1) / csa::kTileEntries);
             if (!scores && c.rows <= csa::kStreamRows && tiles_bound < 0x7FFFFFFF)

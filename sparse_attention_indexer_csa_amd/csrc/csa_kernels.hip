@@ -34,6 +34,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, int
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
 }
 
+// Bytes a buffer resource must cover for n consecutive entries of D bf16 at
+// a stride of entry_bytes: from the first entry's start to the end of the
+// last entry's D values.  Strides below the row width (overlapping entries,
+// or 0 for a single entry) are covered as well as padded ones.  16-byte
+// slots past that range (row pads) read zeros and are never consumed.
+template <int D>
+__device__ __forceinline__ int entries_span(int n, int entry_bytes)
+{
+    return n > 0 ? (n - 1) * entry_bytes + 2 * D : 0;
+}
+
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voffset)
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
@@ -176,7 +187,7 @@ void rows_kernel(const KernelArgs a)
     auto fetch = [&](int t) {
         const int e0 = t * kTileEntries;
         const int n = min(W - e0, kTileEntries);
-        const __amdgpu_buffer_rsrc_t r = raw_rsrc(kb + t * tile_stride, n * entry_bytes);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(kb + t * tile_stride, entries_span<D>(n, entry_bytes));
         unsigned char *dst = smem + (size_t)(t & 1) * G::kTileBytes + wv * kWave * 16;
 #pragma unroll
         for (int x = 0; x < kFullOps; ++x)
@@ -354,7 +365,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(const Kernel
     auto dma_subtile = [&](int sub) {
         const int e0 = base + sub * 32;
         const int n = max(0, min(32, thr - e0));
-        const __amdgpu_buffer_rsrc_t r = raw_rsrc(kb + (int64_t)e0 * a.k_sw, n * entry_bytes);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(kb + (int64_t)e0 * a.k_sw, entries_span<D>(n, entry_bytes));
         unsigned char *dst = wbuf + (sub & 1) * G::kBufBytes;
 #pragma unroll
         for (int x = 0; x < G::kDmaOps; ++x) {
@@ -535,7 +546,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void stream_kernel(const Kerne
         const int b = dc.row / a.S;
         const int e0 = (t - dc.rs) * kTileEntries + (sub & 1) * 32;
         const int n = max(0, min(32, thr_of[dc.row] - e0));
-        const __amdgpu_buffer_rsrc_t r = raw_rsrc(a.k + b * a.k_sb + (int64_t)e0 * a.k_sw, n * entry_bytes);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(a.k + b * a.k_sb + (int64_t)e0 * a.k_sw, entries_span<D>(n, entry_bytes));
         unsigned char *dst = wbuf + (sub & 1) * G::kBufBytes;
 #pragma unroll
         for (int x = 0; x < G::kDmaOps; ++x) {

@@ -578,19 +578,23 @@ __device__ __forceinline__ bool sort_and_write_fast(const uint32_t *key, const E
 #pragma unroll
     for (int r = 0; r < E; ++r) {
         const int e = l * E + r;
-        // empty slots are 0; a valid element has position bits >= 1 (e < n <= 64E)
+        // empty slots are 0.  A valid composite is 0 only for the element at
+        // e = 64E-1 with a key in the lowest bucket, and then n = 64E and no
+        // slot is empty, so after the sort the n valid elements hold sorted
+        // positions 0 .. n-1 in every case.
         c[r] = e < n ? (((kr[r] - kmin) >> shift) << PB) | (kPosMask - (uint32_t)e) : 0u;
     }
     bitonic32_levels<E, 2>(c, l);
     if (shift > 0) {
-        // adjacent elements whose truncated keys are equal must have equal keys
+        // adjacent elements whose truncated keys are equal must have equal
+        // keys; a pair takes part when both its sorted positions are below n
         bool bad = false;
         const uint32_t next0 = from_next_lane(c[0]);
 #pragma unroll
         for (int r = 0; r < E; ++r) {
             const uint32_t a = c[r], b = (r + 1 < E) ? c[r + 1] : next0;
-            const bool pair_in = (r + 1 < E) || l + 1 < kWave;
-            if (pair_in && b != 0u && (a >> PB) == (b >> PB))
+            const bool pair_in = l * E + r + 1 < n;
+            if (pair_in && (a >> PB) == (b >> PB))
                 bad = bad || key[kPosMask - (a & kPosMask)] != key[kPosMask - (b & kPosMask)];
         }
         if (ballot(bad) != 0ull)

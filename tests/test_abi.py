@@ -234,3 +234,36 @@ def test_backward_workspace_and_validation(lib):
     assert call(pp=prob(D=40)) == UNSUPPORTED
     assert call(pp=prob(H=130)) == UNSUPPORTED
     assert call(pp=prob(B=0), q=0, k=0, w=0, g=0, dq=0, dk=0, dw=0, ws=0, wsb=0) == OK
+
+
+def test_binding_refuses_short_mask_tensors():
+    """Every mask element is read by the kernels, so the binding checks the
+    full shapes before anything reaches the library: a k_seg shorter than W
+    (or a q_seg shorter than S, a q_offset shorter than B) is refused."""
+    import torch
+    B, S, W = 2, 16, 8
+    seg_q = torch.zeros(B, S, dtype=torch.int32)
+    seg_k = torch.zeros(B, W, dtype=torch.int32)
+    csa.check_mask_shapes(B, S, W, torch.zeros(B, dtype=torch.int32), seg_q, seg_k)
+    with pytest.raises(ValueError, match="k_seg"):
+        csa.check_mask_shapes(B, S, W, None, seg_q, torch.zeros(B, W - 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="k_seg"):
+        csa.check_mask_shapes(B, S, W, None, seg_q, torch.zeros(B, W + 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="q_seg"):
+        csa.check_mask_shapes(B, S, W, None, torch.zeros(B, S - 1, dtype=torch.int32), seg_k)
+    with pytest.raises(ValueError, match="q_offset"):
+        csa.check_mask_shapes(B, S, W, torch.zeros(B - 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="int32"):
+        csa.check_mask_shapes(B, S, W, None, seg_q, seg_k.long())
+    with pytest.raises(ValueError, match="together"):
+        csa.check_mask_shapes(B, S, W, None, seg_q, None)
+    with pytest.raises(ValueError, match="contiguous"):
+        csa.check_mask_shapes(B, S, W, None, seg_q, torch.zeros(B, 2 * W, dtype=torch.int32)[:, ::2])
+
+
+def test_key_stride_below_row_width_is_accepted(lib):
+    """Entries may overlap (0 < k_sw < D) or repeat (k_sw = 0, which the
+    binding passes for a one-entry cache): only multiples of 8 are required."""
+    for k_sw in (0, 8, 16):
+        st, _ = ws_size(lib, prob(D=32, k_sw=k_sw), 4)
+        assert st == OK, lib.csa_last_error()

@@ -372,3 +372,108 @@ def test_balanced_split_exact(case):
     assert_topk_match(idx, i_o, s_o, exact=True, what=f"{case}")
     idx2, _ = gpu_select(P, plan="split_rows", dev=d, return_scores=True)
     np.testing.assert_array_equal(to_np(idx2).reshape(P.rows, -1), idx)
+
+
+# --- key strides below the row width, one-entry caches ----------------------------------------
+
+@pytest.mark.parametrize("plan", PLANS)
+def test_one_entry_cache_exact(plan):
+    """W = 1: the binding passes the stride of a size-1 dimension as 0, so the
+    key tile covers a single 2*D-byte entry; scores and selections equal the
+    oracle's bit for bit."""
+    for B, S, H, D in ((2, 9, 16, 32), (1, 40, 64, 128)):
+        P = make_problem(B, S, H, D, 1, 1, 3, dist="int", seed=B * S + H)
+        s_o, i_o = oracle.select(P)
+        idx, sc = gpu_select(P, plan=plan, return_scores=True)
+        assert_scores_close(to_np(sc).reshape(P.rows, 1), s_o, exact=True, what=f"W=1 {plan}")
+        assert_topk_match(to_np(idx).reshape(P.rows, -1), i_o, s_o, exact=True, what=f"W=1 {plan}")
+        assert_scores_close(to_np(gpu_score(P, plan=plan)).reshape(P.rows, 1), s_o, exact=True, what="W=1 score")
+        assert_topk_match(to_np(gpu_select(P, plan=plan)).reshape(P.rows, -1), i_o, s_o, exact=True,
+                          what=f"W=1 {plan} select only")
+
+
+@pytest.mark.parametrize("plan", PLANS)
+def test_overlapping_key_rows_exact(plan):
+    """Entry j of k read at j * k_sw with k_sw (8 or 0 elements) below D: the
+    entries overlap in memory.  The oracle gets the same entries written out
+    densely; every kernel must read exactly those bytes."""
+    B, S, H, D, W, m, k = 2, 64, 16, 32, 24, 2, 6
+    for k_sw in (8, 0):
+        P = make_problem(B, S, H, D, W, m, k, dist="int", seed=70 + k_sw)
+        flat = P.k.reshape(B, -1)[:, :(W - 1) * k_sw + D]
+        P.k = np.ascontiguousarray(np.stack([np.stack([flat[b, j * k_sw:j * k_sw + D] for j in range(W)])
+                                             for b in range(B)]))
+        s_o, i_o = oracle.select(P)
+        d = dev_problem(P)
+        base = torch.from_numpy(np.ascontiguousarray(flat).view(np.int16)).view(torch.bfloat16).cuda()
+        d["k"] = torch.as_strided(base, (B, W, D), (base.stride(0), k_sw, 1))
+        idx, sc = gpu_select(P, plan=plan, dev=d, return_scores=True)
+        assert_scores_close(to_np(sc).reshape(P.rows, W), s_o, exact=True, what=f"k_sw={k_sw} {plan}")
+        assert_topk_match(to_np(idx).reshape(P.rows, -1), i_o, s_o, exact=True, what=f"k_sw={k_sw} {plan}")
+        assert_topk_match(to_np(gpu_select(P, plan=plan, dev=d)).reshape(P.rows, -1), i_o, s_o, exact=True,
+                          what=f"k_sw={k_sw} {plan} select only")
+
+
+def test_short_segment_ids_refused():
+    P = make_problem(1, 64, 16, 32, 16, 4, 4, dist="int", seed=3, segments="random")
+    d = dev_problem(P)
+    d["k_seg"] = d["k_seg"][:, :-1].contiguous()
+    with pytest.raises(ValueError, match="k_seg"):
+        gpu_select(P, dev=d)
+
+
+def test_sort_of_full_buffer_with_lowest_bucket_last():
+    """A row with exactly 512 selectable entries and k = 512 is sorted by the
+    32-bit composite sort with nine position bits.  Its last entry holds a key
+    in the lowest truncated bucket, just above the smallest key: its composite
+    is 0 and the truncation check must still compare it with its neighbour,
+    so the output order is exact."""
+    s = (100.0 + np.arange(512)).astype(np.float32)
+    s[0] = 1.0
+    s[511] = np.float32(1.0) + np.float32(3 * 2.0 ** -23)
+    rows = np.stack([s, s[::-1].copy()])
+    want = oracle.topk(rows, 512)
+    assert want[0, -2] == 511 and want[0, -1] == 0
+    np.testing.assert_array_equal(to_np(csa.topk(torch.from_numpy(rows).cuda(), 512)), want)
+
+
+# --- scales other than 1, compared element-wise with the oracle --------------------------------
+
+@pytest.mark.parametrize("scale", [0.08838835, -1.0, 3.7])
+@pytest.mark.parametrize("plan", PLANS)
+def test_scale_elementwise(scale, plan):
+    """The scale is one fp32 multiply after the head sum: on the integer grid
+    the unscaled sum is exact, so the oracle's scaled scores (1/sqrt(128),
+    -1, 3.7) and selections are matched bit for bit; on Gaussian inputs
+    within the tolerance."""
+    for dist in ("int", "gauss"):
+        P = make_problem(2, 300, 64, 128, 75, 4, 24, dist=dist, seed=57, scale=scale)
+        s_o, i_o = oracle.select(P)
+        idx, sc = gpu_select(P, plan=plan, return_scores=True)
+        exact = dist == "int"
+        assert_scores_close(to_np(sc).reshape(P.rows, P.W), s_o, exact=exact, what=f"{dist} scale={scale}")
+        assert_topk_match(to_np(idx).reshape(P.rows, -1), i_o, s_o, exact=exact, what=f"{dist} scale={scale}")
+        assert_topk_match(to_np(gpu_select(P, plan=plan)).reshape(P.rows, -1), i_o, s_o, exact=exact,
+                          what=f"{dist} scale={scale} select only")
+
+
+def test_long_prefill_integer_grid_sampled():
+    """The seq-16384 prefill shape (S=16384, H=64, D=128, W=4096, k=512) on the
+    integer grid (seed 33), in the benchmark's launch configuration (fused
+    select without a score output).  Rows past 6144 see more than the 1536
+    pairs the row kernel's buffer holds, so its mid-stream compactions run,
+    here under heavy ties: 72 sampled rows must equal the oracle bit for bit,
+    scores (from the score call) and selections."""
+    P = make_problem(1, 16384, 64, 128, 4096, 4, 512, dist="int", seed=33, name="c3int")
+    d = dev_problem(P)
+    assert csa.resolve_plan(d["q"], d["k"], d["w"], P.m) == "row_tiles"
+    idx = to_np(gpu_select(P, dev=d)).reshape(P.rows, -1)
+    sc = to_np(gpu_score(P, dev=d)).reshape(P.rows, P.W)
+    rng = np.random.default_rng(33)
+    rows = np.unique(np.concatenate([[3, 4, 2047, 2048, 6143, 6144, 6147, 16382, 16383],
+                                     rng.choice(np.arange(6148, 16382), 48, replace=False),
+                                     rng.choice(np.arange(5, 6143), 16, replace=False)])).astype(np.int64)
+    assert len(rows) >= 64
+    s_o, i_o = oracle.select(P, rows)
+    assert_scores_close(sc[rows], s_o, exact=True, what="c3int score")
+    assert_topk_match(idx[rows], i_o, s_o, exact=True, what="c3int select")

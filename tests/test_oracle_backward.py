@@ -149,44 +149,129 @@ def test_masked_gradient_is_ignored():
         np.testing.assert_array_equal(a, b)
 
 
-def test_bounds_are_small_and_cover_undecided_signs():
-    """The per-element bounds are non-negative, a small fraction of the
-    absolute sums for Gaussian inputs, and include the whole term when a
-    logit is exactly zero (its indicator is undecided in float32)."""
+def test_statistics_cover_undecided_signs():
+    """The per-element statistics are non-negative, and a logit of exactly
+    zero (its ReLU derivative is undecided in float32) puts the whole term in
+    the undecided mass and none of it in the decided sums."""
     P, g = _problem(15)
-    dq, dk, dw, bq, bk, bw = oracle.backward(P, g, bounds=True)
-    for b in (bq, bk, bw):
-        assert np.all(b >= 0)
-    # A zero logit: q row 0 of head 0 orthogonal to every key -> logit 0 for
-    # every entry, so dq[0,0,i] gets no term but its bound gets all of them.
-    S = P.S
-    i = S - 1
+    dq, dk, dw, sq, sk, sw = oracle.backward(P, g, stats=True)
+    for s in (sq, sk, sw):
+        assert np.all(s >= 0)
+    # q row i of head 0 set to zero: logit 0 for every entry, so dq[0,0,i]
+    # gets no term and its undecided mass gets all of them
+    i = P.S - 1
     q = _f64(P.q).copy()
     q[0, 0, i] = 0.0
     P.q = f32_to_bf16_bits(q.astype(np.float32))
-    dq, dk, dw, bq, bk, bw = oracle.backward(P, g, bounds=True)
+    dq, dk, dw, sq, sk, sw = oracle.backward(P, g, stats=True)
     assert np.all(dq[0, 0, i] == 0.0)
+    assert np.all(sq[0, 0, i, :, 0] == 0.0) and np.all(sq[0, 0, i, :, 1] == 0.0)
     nvis = int(_mask(P)[0, i].sum())
     kf = _f64(P.k)[0, :nvis]
     wv = float(_f64(P.w)[0, i, 0])
     expect = np.sum(np.abs(g[0, i, :nvis, None].astype(np.float64) * wv * kf), axis=0)
-    np.testing.assert_allclose(bq[0, 0, i], expect, rtol=1e-12)
+    np.testing.assert_allclose(sq[0, 0, i, :, 2], expect, rtol=1e-12)
+    # the decided sums of another row are the sums of |term| and term^2
+    # over its positive logits
+    i2 = 20
+    nv2 = int(_mask(P)[0, i2].sum())
+    qh = _f64(P.q)[0, 0, i2]
+    lg = _f64(P.k)[0, :nv2] @ qh
+    t = (g[0, i2, :nv2].astype(np.float64) * float(_f64(P.w)[0, i2, 0]))[:, None] * _f64(P.k)[0, :nv2]
+    pos = lg > 0
+    np.testing.assert_allclose(sq[0, 0, i2, :, 0], np.abs(t[pos]).sum(axis=0), rtol=1e-12)
+    np.testing.assert_allclose(sq[0, 0, i2, :, 1], (t[pos] ** 2).sum(axis=0), rtol=1e-12)
 
 
 def test_sampled_rows_and_entries_equal_the_full_backward():
     """backward_sample (used at sizes where the full backward is too slow)
     returns the full backward's values at the chosen rows and entries."""
     P, g = _problem(16, segments="random", S=48)
-    dq, dk, dw, bq, bk, bw = oracle.backward(P, g, bounds=True)
+    dq, dk, dw, sq, sk, sw = oracle.backward(P, g, stats=True)
     rows = [0, 5, P.S + 47, 2 * P.S - 1]
     ents = [0, 3, P.W + 11]
-    sq, sw, sk, sbq, sbw, sbk = oracle.backward_sample(P, g, rows, ents)
+    xq, xw, xk, yq, yw, yk = oracle.backward_sample(P, g, rows, ents)
     for r, row in enumerate(rows):
         b, i = divmod(row, P.S)
-        np.testing.assert_array_equal(sq[r], dq[b, :, i, :])
-        np.testing.assert_array_equal(sw[r], dw[b, i])
-        np.testing.assert_array_equal(sbq[r], bq[b, :, i, :])
+        np.testing.assert_array_equal(xq[r], dq[b, :, i, :])
+        np.testing.assert_array_equal(xw[r], dw[b, i])
+        np.testing.assert_array_equal(yq[r], sq[b, :, i, :])
+        np.testing.assert_array_equal(yw[r], sw[b, i])
     for e, ent in enumerate(ents):
         b, j = divmod(ent, P.W)
-        np.testing.assert_array_equal(sk[e], dk[b, j])
-        np.testing.assert_array_equal(sbk[e], bk[b, j])
+        np.testing.assert_array_equal(xk[e], dk[b, j])
+        np.testing.assert_array_equal(yk[e], sk[b, j])
+
+
+# --- the bounds at the seq-16384 shape: a float32 emulation passes, planted mistakes fail ---
+
+CHUNK = 256  # rows per partial key gradient in the emulated implementation
+
+
+def _bf16(x):
+    return bf16_bits_to_f32(f32_to_bf16_bits(np.asarray(x, np.float32)))
+
+
+def _emulate_dq(P, g, i, g_row):
+    """dq of row i the way an fp32 kernel computes it: fp32 logits, the
+    operand g [l > 0] rounded to bf16, an fp32 product with the keys, then
+    scale * w.  g_row selects whose upstream gradient is used (i, or another
+    row to plant a mistake)."""
+    n = min((i + 1) // P.m, P.W)
+    q = bf16_bits_to_f32(P.q[0, :, i, :])
+    k = bf16_bits_to_f32(P.k[0, :n, :])
+    lg = q @ k.T
+    a = np.where(lg > 0, _bf16(g[0, g_row, :n])[None, :], np.float32(0)).astype(np.float32)
+    f = (np.float32(P.scale) * bf16_bits_to_f32(P.w[0, i, :])).astype(np.float32)
+    return f[:, None] * (a @ k)
+
+
+def _emulate_dk(P, g, j, drop_chunk=None):
+    """dk of entry j the way a chunked fp32 kernel computes it: per chunk of
+    CHUNK rows the operands g w [l > 0] (fp32 product rounded to bf16)
+    contracted with q in fp32, the chunk partials added in order, times the
+    scale.  drop_chunk plants a lost partial.  Returns (dk, live chunks)."""
+    i0 = (j + 1) * P.m - 1
+    k = bf16_bits_to_f32(P.k[0, j])
+    acc = np.zeros(P.D, np.float32)
+    live = []
+    for c in range((P.S + CHUNK - 1) // CHUNK):
+        r0, r1 = max(c * CHUNK, i0), min((c + 1) * CHUNK, P.S)
+        if r0 >= r1:
+            continue
+        live.append(c)
+        Q = bf16_bits_to_f32(P.q[0, :, r0:r1, :])
+        lg = Q @ k
+        gw = (g[0, r0:r1, j][None, :] * bf16_bits_to_f32(P.w[0, r0:r1, :]).T).astype(np.float32)
+        op = np.where(lg > 0, _bf16(gw), np.float32(0)).astype(np.float32)
+        part = op.reshape(-1) @ Q.reshape(-1, P.D)
+        if c != drop_chunk:
+            acc = (acc + part).astype(np.float32)
+    return np.float32(P.scale) * acc, live
+
+
+@pytest.mark.slow
+def test_bounds_at_seq16384_pass_emulation_and_catch_planted_mistakes():
+    """At the seq-16384 shape (S=16384, H=64, D=128, W=4096), on sampled rows
+    (255, 256, 9999) and entries (0, 127, 128, 1000), the bounds that the GPU
+    backward is held to (sum lengths W for dq, CHUNK*H plus the chunk count
+    for dk) admit a float32 emulation of the kernel's rounding everywhere,
+    and reject most elements of two planted mistakes: dq computed with the
+    next row's upstream gradient, and dk with one chunk's partial dropped."""
+    from synth import make_config
+    P = make_config("c3")
+    g = np.random.default_rng(9).standard_normal((P.B, P.S, P.W)).astype(np.float32)
+    rows, ents = [255, 256, 9999], [0, 127, 128, 1000]
+    dq, dw, dk, sq, sw, sk = oracle.backward_sample(P, g, rows, ents)
+    bq = oracle.error_bounds(dq, sq, P.W, True)
+    bk = oracle.error_bounds(dk, sk, CHUNK * P.H + P.S // CHUNK, True)
+    for r, i in enumerate(rows):
+        assert np.all(np.abs(_emulate_dq(P, g, i, i) - dq[r]) <= bq[r]), f"emulated dq row {i}"
+        bad = np.abs(_emulate_dq(P, g, i, i + 1) - dq[r]) > bq[r]
+        assert bad.mean() > 0.9, f"swapped gradient rows: only {bad.mean():.2f} of row {i} rejected"
+    for e, j in enumerate(ents):
+        got, live = _emulate_dk(P, g, j)
+        assert np.all(np.abs(got - dk[e]) <= bk[e]), f"emulated dk entry {j}"
+        dropped, _ = _emulate_dk(P, g, j, drop_chunk=live[len(live) // 2])
+        bad = np.abs(dropped - dk[e]) > bk[e]
+        assert bad.mean() > 0.4, f"dropped chunk partial: only {bad.mean():.2f} of entry {j} rejected"
