@@ -130,6 +130,27 @@ csa_status csa_index_select(const csa_index_problem *p, const void *q, const voi
 csa_status csa_index_workspace_size(const csa_index_problem *p, int32_t top_k, size_t *bytes);
 
 /*
+ * csa_index_select without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The workspace csa_index_select would take
+ * comes from a scratch buffer of CSA_NOALLOC_SCRATCH_BYTES that the library
+ * holds in device memory, one per GPU, from the first call on that GPU until
+ * the process ends; this function allocates and frees nothing.  Problems
+ * whose workspace (csa_index_workspace_size) exceeds it return
+ * CSA_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU
+ * shares that GPU's buffer, so calls that overlap on one GPU (concurrent
+ * streams, or host threads without ordering) race and must not be issued;
+ * calls ordered on one stream are safe.  The kernels overwrite every part of
+ * the buffer they later read, so no call depends on an earlier one's
+ * contents.  Arguments and results are those of csa_index_select.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+csa_status csa_index_select_noalloc(const csa_index_problem *p, const void *q, const void *k, const void *w,
+                                    const csa_index_masks *masks, int32_t top_k, int32_t *idx, float *scores,
+                                    void *stream);
+
+/*
  * Backward of csa_index_score: the gradients of
  *     L = sum over unmasked (b,i,j) of grad[b,i,j] * score[b,i,j]
  * with respect to q, k and w (the vector-Jacobian product of the custom VJP

@@ -68,6 +68,7 @@ SIGNATURES = {
     "csa_index_topk_workspace_size": (_I32, [_I64, _I32, _I32, ctypes.POINTER(_SZ)]),
     "csa_index_select": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "csa_index_workspace_size": (_I32, [_VP, _I32, ctypes.POINTER(_SZ)]),
+    "csa_index_select_noalloc": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
     "csa_index_resolve_plan": (_I32, [_VP]),
     "csa_index_score_backward": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "csa_index_backward_workspace_size": (_I32, [_VP, ctypes.POINTER(_SZ)]),
@@ -284,6 +285,34 @@ def select(q, k, w, top_k: int, compress_rate: int, scale: float = 1.0, q_offset
     return (out, sc) if return_scores else out
 
 
+# Bytes of the library's own scratch buffer used by select_noalloc.
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def select_noalloc(q, k, w, top_k: int, compress_rate: int, out: torch.Tensor, scale: float = 1.0, q_offset=None,
+                   q_seg=None, k_seg=None, plan: str = "auto", scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """csa_index_select_noalloc: the fused select writing into the caller's
+    ``out`` [B,S,top_k] int32 (and ``scores`` [B,S,W] fp32 if given), with
+    any workspace taken from the library's fixed per-GPU scratch buffer.
+    Nothing is allocated here or in the library.  Calls that overlap on one
+    GPU race on that buffer."""
+    lib = load_library()
+    p = _problem(q, k, w, compress_rate, scale, plan)
+    m = _masks(q, k, q_offset, q_seg, k_seg)
+    _dev_tensor(out, "out", torch.int32, 3)
+    if tuple(out.shape) != (p.B, p.S, int(top_k)) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 [B,S,top_k] tensor")
+    if scores is not None:
+        _dev_tensor(scores, "scores", torch.float32, 3)
+        if tuple(scores.shape) != (p.B, p.S, p.W) or not scores.is_contiguous():
+            raise ValueError("scores must be a contiguous float32 [B,S,W] tensor")
+    st = lib.csa_index_select_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(w), ctypes.byref(m), int(top_k),
+                                      _ptr(out), _ptr(scores), ctypes.c_void_p(_stream(q.device)))
+    if st != _OK:
+        _raise(st, "csa_index_select_noalloc")
+    return out
+
+
 def backward_workspace_size(q, k, w, compress_rate: int) -> int:
     """Bytes of workspace csa_index_score_backward needs for these tensors."""
     lib = load_library()
@@ -338,6 +367,6 @@ def score_backward(q, k, w, grad, compress_rate: int, scale: float = 1.0, q_offs
     return dq, dk, dw
 
 
-__all__ = ["score", "topk", "select", "score_backward", "workspace_size", "backward_workspace_size",
+__all__ = ["score", "topk", "select", "select_noalloc", "score_backward", "workspace_size", "backward_workspace_size",
            "resolve_plan", "load_library", "CsaIndexError",
            "CsaUnsupportedError", "LIB_PATH", "SIGNATURES", "PLANS"]

@@ -280,6 +280,43 @@ csa_status check_backward(const csa_index_problem *p, Checked &c, csa_index_prob
     return CSA_OK;
 }
 
+// Fixed device scratch of csa_index_select_noalloc: one copy per GPU, held
+// until the process ends.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in for the symbol); each device's
+// address comes from hipGetSymbolAddress, taken once with that device
+// current.
+constexpr size_t kNoAllocScratchBytes = CSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mutex;
+std::atomic<bool> g_scratch_ready[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices]; // written once, under the mutex, before its flag is set
+
+// Address of the current device's copy of `scratch`.
+csa_status scratch_for_current_device(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(CSA_ERR_DEVICE, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(CSA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table holds", dev,
+                    kMaxDevices);
+    if (!g_scratch_ready[dev].load(std::memory_order_acquire)) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        if (!g_scratch_ready[dev].load(std::memory_order_relaxed)) {
+            void *ptr = nullptr;
+            hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || ptr == nullptr)
+                return fail(CSA_ERR_DEVICE, "cannot resolve the scratch buffer on device %d: %s", dev,
+                            hipGetErrorString(e));
+            g_scratch_ptr[dev] = ptr;
+            g_scratch_ready[dev].store(true, std::memory_order_release);
+        }
+    }
+    *out = g_scratch_ptr[dev];
+    return CSA_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -454,6 +491,31 @@ csa_status csa_index_select(const csa_index_problem *p, const void *q, const voi
         return st;
     a.scores = scores;
     return launched(csa::launch_rows(p->D, c.HB, mode, a, lds, s), "row-tile select");
+}
+
+csa_status csa_index_select_noalloc(const csa_index_problem *p, const void *q, const void *k, const void *w,
+                                    const csa_index_masks *masks, int32_t top_k, int32_t *idx, float *scores,
+                                    void *stream)
+{
+    Checked c;
+    csa_status st = check_problem(p, c);
+    if (st != CSA_OK)
+        return st;
+    if (top_k < 1 || top_k > kMaxTopK)
+        return fail(CSA_ERR_UNSUPPORTED, "top_k=%d outside [1, %d]", top_k, kMaxTopK);
+    // the workspace csa_index_select would take (none with a score output)
+    const size_t need = scores ? 0 : select_workspace(p, c);
+    if (need > kNoAllocScratchBytes)
+        return fail(CSA_ERR_WORKSPACE,
+                    "this problem needs %zu bytes of workspace, above the %zu-byte scratch of the "
+                    "no-allocation entry point (use csa_index_select with a workspace)",
+                    need, kNoAllocScratchBytes);
+    if (need == 0)
+        return csa_index_select(p, q, k, w, masks, top_k, idx, scores, nullptr, 0, stream);
+    void *ws = nullptr;
+    if ((st = scratch_for_current_device(&ws)) != CSA_OK)
+        return st;
+    return csa_index_select(p, q, k, w, masks, top_k, idx, scores, ws, kNoAllocScratchBytes, stream);
 }
 
 csa_status csa_index_backward_workspace_size(const csa_index_problem *p, size_t *bytes)

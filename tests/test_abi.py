@@ -267,3 +267,20 @@ def test_key_stride_below_row_width_is_accepted(lib):
     for k_sw in (0, 8, 16):
         st, _ = ws_size(lib, prob(D=32, k_sw=k_sw), 4)
         assert st == OK, lib.csa_last_error()
+
+
+def test_noalloc_refuses_oversized_workspace_on_the_host(lib):
+    """The no-allocation select checks the problem's workspace against its
+    fixed scratch (16 MiB) before touching the device."""
+    assert csa.NOALLOC_SCRATCH_BYTES == 16 << 20
+    p = prob(B=128, S=1, H=4, D=32, W=40000, plan=2)
+    st, need = ws_size(lib, p, 16)
+    assert st == OK and need > csa.NOALLOC_SCRATCH_BYTES
+    m = masks()
+    f = ctypes.c_void_p(FAKE)
+    st = lib.csa_index_select_noalloc(ctypes.byref(p), f, f, f, ctypes.byref(m), 16, f, None, None)
+    assert st == WORKSPACE
+    assert b"scratch" in lib.csa_last_error()
+    assert lib.csa_index_select_noalloc(None, f, f, f, ctypes.byref(m), 16, f, None, None) == INVALID
+    assert lib.csa_index_select_noalloc(ctypes.byref(prob()), f, f, f, ctypes.byref(m), 0, f, None, None) \
+        == UNSUPPORTED
