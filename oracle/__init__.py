@@ -62,6 +62,8 @@ def _load():
     lib.csa_oracle_backward_f64.restype = None
     lib.csa_oracle_backward_sample_f64.argtypes = [i64] * 6 + [f64] + [vp] * 7 + [i64, vp, i64, vp] + [vp] * 6
     lib.csa_oracle_backward_sample_f64.restype = None
+    lib.csa_oracle_kl_from_scores.argtypes = [i64, i64, vp, vp, vp, vp, vp]
+    lib.csa_oracle_kl_from_scores.restype = None
     lib.csa_oracle_version.restype = ctypes.c_int
     lib.csa_oracle_threads.restype = ctypes.c_int
     _lib = lib
@@ -250,3 +252,37 @@ def error_bounds(value: np.ndarray, stats: np.ndarray, n: int, bf16_operand: boo
     if bf16_operand:
         b = b + LAMBDA * (U_BF16 + 2 * U_F32) * np.sqrt(r2)
     return b
+
+
+def kl_from_scores(score_rows: np.ndarray, target: np.ndarray, grad: bool = False, magnitudes: bool = False):
+    """KL(target || softmax(scores)) per row over the visible entries
+    (scores -inf where masked), the target normalised over those entries;
+    see csa_oracle.c.  score_rows [rows, W] (taken as float64), target
+    [rows, W] float32.  Returns kl [rows] float64, then grad [rows, W]
+    (d kl / d score) and magnitudes [rows, 3] if asked."""
+    s = np.ascontiguousarray(score_rows, dtype=np.float64)
+    a = np.ascontiguousarray(target, dtype=np.float32)
+    if s.ndim != 2 or a.shape != s.shape:
+        raise ValueError("scores and target must both be [rows, W]")
+    kl = np.empty(s.shape[0], np.float64)
+    g = np.empty(s.shape, np.float64) if grad else None
+    mg = np.empty((s.shape[0], 3), np.float64) if magnitudes else None
+    _load().csa_oracle_kl_from_scores(s.shape[0], s.shape[1], _ptr(s), _ptr(a), _ptr(kl), _ptr(g), _ptr(mg))
+    out = (kl,)
+    if grad:
+        out += (g,)
+    if magnitudes:
+        out += (mg,)
+    return out if len(out) > 1 else kl
+
+
+def kl_loss(P, target: np.ndarray, rows: Optional[Sequence[int]] = None, grad: bool = False,
+            magnitudes: bool = False):
+    """The indexer KL loss of the given rows (b*S+i): the oracle's float32
+    scores of those rows, then kl_from_scores with the rows' targets.
+    target is [B, S, W]."""
+    s = scores(P, rows)
+    t = np.asarray(target, dtype=np.float32).reshape(P.B * P.S, P.W)
+    if rows is not None:
+        t = t[np.asarray(rows, dtype=np.int64).reshape(-1)]
+    return kl_from_scores(s, t, grad=grad, magnitudes=magnitudes)

@@ -420,7 +420,85 @@ void csa_oracle_backward_sample_f64(int64_t B, int64_t S, int64_t H, int64_t D, 
                        g, &dk[e * D], sk ? &sk[e * D * 3] : NULL);
 }
 
-int csa_oracle_version(void) { return 2; }
+/*
+ * Indexer loss: the KL divergence between a target distribution over a
+ * row's entries and the softmax of the row's indexer scores (the loss that
+ * MaxText PR #4564 "Implement QK attention head chunking in MLA" computes in
+ * calculate_indexer_loss and chunks over heads).  The pages give no formula;
+ * the reading taken is
+ *
+ *   p_j   = a_j / A,  A = sum over visible j of a_j   (a = caller's target, >= 0)
+ *   lse   = log sum over visible j of exp(s_j)
+ *   KL_i  = sum over visible j with p_j > 0 of p_j (log p_j - (s_j - lse))
+ *   dKL_i/ds_j = exp(s_j - lse) - p_j   (visible j), 0 (masked j)
+ *
+ * over the entries j the row can see (the causal and segment masks of the
+ * score).  Rows with no visible entry or zero target mass have KL = 0 and a
+ * zero gradient.  Target values at masked positions are never read into a
+ * result.
+ *
+ * csa_oracle_kl_from_scores works on given float64 scores [rows, W] (-inf =
+ * masked) and float32 targets [rows, W]; kl [rows] and grad [rows, W] (NULL =
+ * not computed) are float64.  mag [rows, 3] (NULL = not computed) receives
+ * the magnitudes a float32 evaluation rounds against: sum p |log p|,
+ * sum p |s|, |lse|.
+ */
+void csa_oracle_kl_from_scores(int64_t rows, int64_t W, const double *scores, const float *target, double *kl,
+                               double *grad, double *mag)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *s = &scores[r * W];
+        const float *a = &target[r * W];
+        double smax = -INFINITY, A = 0.0;
+        int64_t nvis = 0;
+        for (int64_t j = 0; j < W; ++j) {
+            if (s[j] == -INFINITY)
+                continue;
+            ++nvis;
+            if (s[j] > smax)
+                smax = s[j];
+            A += (double)a[j];
+        }
+        double *gr = grad ? &grad[r * W] : NULL;
+        if (nvis == 0 || !(A > 0.0)) {
+            kl[r] = 0.0;
+            if (gr)
+                for (int64_t j = 0; j < W; ++j)
+                    gr[j] = 0.0;
+            if (mag)
+                mag[3 * r] = mag[3 * r + 1] = mag[3 * r + 2] = 0.0;
+            continue;
+        }
+        double sumexp = 0.0;
+        for (int64_t j = 0; j < W; ++j)
+            if (s[j] != -INFINITY)
+                sumexp += exp(s[j] - smax);
+        double lse = smax + log(sumexp);
+        double acc = 0.0, m_plogp = 0.0, m_ps = 0.0;
+        for (int64_t j = 0; j < W; ++j) {
+            if (s[j] == -INFINITY)
+                continue;
+            double pj = (double)a[j] / A;
+            if (pj > 0.0) {
+                acc += pj * (log(pj) - (s[j] - lse));
+                m_plogp += pj * fabs(log(pj));
+                m_ps += pj * fabs(s[j]);
+            }
+        }
+        kl[r] = acc;
+        if (mag) {
+            mag[3 * r] = m_plogp;
+            mag[3 * r + 1] = m_ps;
+            mag[3 * r + 2] = fabs(lse);
+        }
+        if (gr)
+            for (int64_t j = 0; j < W; ++j)
+                gr[j] = s[j] == -INFINITY ? 0.0 : exp(s[j] - lse) - (double)a[j] / A;
+    }
+}
+
+int csa_oracle_version(void) { return 3; }
 
 /* OpenMP threads the oracle's parallel loops use. */
 int csa_oracle_threads(void) { return omp_get_max_threads(); }
