@@ -179,6 +179,29 @@ csa_status csa_index_score_backward(const csa_index_problem *p, const void *q, c
                                     const csa_index_masks *masks, const float *grad, float *dq, float *dk,
                                     float *dw, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Indexer loss: per query row, the KL divergence between a target
+ * distribution over the row's visible entries and the softmax of the row's
+ * scores (the KL-divergence loss of calculate_indexer_loss in MaxText PR #4564
+ * "Implement QK attention head chunking in MLA", there chunked over heads;
+ * here the score's 32-head blocks are the chunks).  The pages give no
+ * formula; with the masks of csa_index_score, a = target[b,i,:] and visible j:
+ *     p_j   = a_j / sum_j a_j              (the target, L1-normalised)
+ *     kl[b,i] = sum_j p_j (log p_j - log softmax(score[b,i,:])_j),  0 log 0 = 0
+ *     grad[b,i,j] = d kl[b,i] / d score[b,i,j] = softmax_j - p_j  (0 if masked)
+ * Rows with no visible entry or zero target mass get kl = 0 and a zero
+ * gradient.  target: [B,S,W] fp32, dense, >= 0 at visible entries (any value
+ * at masked ones, never read into a result).  kl: [B,S] fp32.  grad: NULL or
+ * [B,S,W] fp32 dense; with NULL the scores never reach HBM (one fused pass
+ * with an online log-sum-exp), otherwise the scores are written to grad and
+ * then turned into the gradient in place (feed it to
+ * csa_index_score_backward for dq, dk, dw).  p->plan is not used.
+ * Computed in fp32 with fast exp/log.
+ */
+csa_status csa_index_kl_loss(const csa_index_problem *p, const void *q, const void *k, const void *w,
+                             const csa_index_masks *masks, const float *target, float *kl, float *grad,
+                             void *stream);
+
 /* Workspace bytes csa_index_score_backward needs for this problem.  Host-only;
  * checks the problem like the call. */
 csa_status csa_index_backward_workspace_size(const csa_index_problem *p, size_t *bytes);

@@ -69,6 +69,7 @@ SIGNATURES = {
     "csa_index_select": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "csa_index_workspace_size": (_I32, [_VP, _I32, ctypes.POINTER(_SZ)]),
     "csa_index_select_noalloc": (_I32, [_VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _VP]),
+    "csa_index_kl_loss": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "csa_index_resolve_plan": (_I32, [_VP]),
     "csa_index_score_backward": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "csa_index_backward_workspace_size": (_I32, [_VP, ctypes.POINTER(_SZ)]),
@@ -313,6 +314,36 @@ def select_noalloc(q, k, w, top_k: int, compress_rate: int, out: torch.Tensor, s
     return out
 
 
+def kl_loss(q, k, w, target, compress_rate: int, scale: float = 1.0, q_offset=None, q_seg=None, k_seg=None,
+            grad: bool = False, out: Optional[torch.Tensor] = None, grad_out: Optional[torch.Tensor] = None):
+    """Indexer loss (csa_index_kl_loss): per row, KL(target || softmax(score))
+    over the visible entries, the target L1-normalised there.  target is
+    [B,S,W] fp32.  Returns kl [B,S] fp32, and with grad=True also
+    d kl / d score [B,S,W] fp32 (input to score_backward)."""
+    lib = load_library()
+    p = _problem(q, k, w, compress_rate, scale, "auto")
+    m = _masks(q, k, q_offset, q_seg, k_seg)
+    dev = q.device
+    _dev_tensor(target, "target", torch.float32, 3)
+    if tuple(target.shape) != (p.B, p.S, p.W) or not target.is_contiguous():
+        raise ValueError("target must be a contiguous [B,S,W] float32 tensor")
+    if out is None:
+        out = torch.empty((p.B, p.S), dtype=torch.float32, device=dev)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (p.B, p.S) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B,S] tensor")
+    g = None
+    if grad:
+        g = grad_out if grad_out is not None else torch.empty((p.B, p.S, p.W), dtype=torch.float32, device=dev)
+        _dev_tensor(g, "grad_out", torch.float32, 3)
+        if tuple(g.shape) != (p.B, p.S, p.W) or not g.is_contiguous():
+            raise ValueError("grad_out must be a contiguous float32 [B,S,W] tensor")
+    st = lib.csa_index_kl_loss(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(w), ctypes.byref(m), _ptr(target),
+                               _ptr(out), _ptr(g), ctypes.c_void_p(_stream(dev)))
+    if st != _OK:
+        _raise(st, "csa_index_kl_loss")
+    return (out, g) if grad else out
+
+
 def backward_workspace_size(q, k, w, compress_rate: int) -> int:
     """Bytes of workspace csa_index_score_backward needs for these tensors."""
     lib = load_library()
@@ -367,6 +398,6 @@ def score_backward(q, k, w, grad, compress_rate: int, scale: float = 1.0, q_offs
     return dq, dk, dw
 
 
-__all__ = ["score", "topk", "select", "select_noalloc", "score_backward", "workspace_size", "backward_workspace_size",
+__all__ = ["score", "topk", "select", "select_noalloc", "kl_loss", "score_backward", "workspace_size", "backward_workspace_size",
            "resolve_plan", "load_library", "CsaIndexError",
            "CsaUnsupportedError", "LIB_PATH", "SIGNATURES", "PLANS"]

@@ -518,6 +518,48 @@ csa_status csa_index_select_noalloc(const csa_index_problem *p, const void *q, c
     return csa_index_select(p, q, k, w, masks, top_k, idx, scores, ws, kNoAllocScratchBytes, stream);
 }
 
+csa_status csa_index_kl_loss(const csa_index_problem *p, const void *q, const void *k, const void *w,
+                             const csa_index_masks *masks, const float *target, float *kl, float *grad,
+                             void *stream)
+{
+    if (!p)
+        return fail(CSA_ERR_INVALID_ARG, "problem descriptor is NULL");
+    // the plan field is not used: the loss runs on the row-tile kernel (any W)
+    csa_index_problem pa = *p;
+    pa.plan = CSA_PLAN_AUTO;
+    Checked c;
+    csa_status st = check_problem(&pa, c);
+    if (st != CSA_OK)
+        return st;
+    if ((st = check_inputs(&pa, c, q, k, w, masks)) != CSA_OK)
+        return st;
+    if (c.rows == 0)
+        return ok();
+    if (c.rows > 0x7FFFFFFF)
+        return fail(CSA_ERR_UNSUPPORTED, "too many rows for one launch");
+    if (!kl || !aligned(kl, 4))
+        return fail(CSA_ERR_INVALID_ARG, "kl must be a non-NULL, 4-byte aligned pointer");
+    if (pa.W > 0 && (!target || !aligned(target, 4)))
+        return fail(CSA_ERR_INVALID_ARG, "target must be a non-NULL, 4-byte aligned pointer");
+    if (grad && !aligned(grad, 4))
+        return fail(CSA_ERR_INVALID_ARG, "grad must be 4-byte aligned");
+    csa::KernelArgs a = make_args(&pa, c, q, k, w, masks);
+    a.target = target;
+    a.kl = kl;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!grad) {
+        const size_t lds = csa::rows_lds_bytes(pa.D, csa::kModeKL, 0);
+        if ((st = device_lds_limit(lds, "row-tile loss")) != CSA_OK)
+            return st;
+        return launched(csa::launch_rows(pa.D, c.HB, csa::kModeKL, a, lds, s), "row-tile loss");
+    }
+    // scores into the gradient buffer, then the loss and its gradient in place
+    if ((st = csa_index_score(&pa, q, k, w, masks, grad, stream)) != CSA_OK)
+        return st;
+    a.scores = grad;
+    return launched(csa::launch_kl_grad(a, s), "loss gradient");
+}
+
 csa_status csa_index_backward_workspace_size(const csa_index_problem *p, size_t *bytes)
 {
     if (!bytes)

@@ -87,6 +87,65 @@ __device__ __forceinline__ float tile_scores(const RowOperand<HB, KS> &row, bool
 }
 
 // ---------------------------------------------------------------------------
+// Indexer KL loss of one row, accumulated over its visible entries: a running
+// maximum m and sum of exp(s - m) (an online log-sum-exp), the target mass A
+// and C = sum of a (log a - s) over entries with target a > 0.  Then
+//   KL = C / A + (m + log sum) - log A,
+// which is sum of p (log p - s + lse) with p = a / A.  A lane holds the
+// statistics of the entries it has seen; kl_merge combines two holders.
+// ---------------------------------------------------------------------------
+struct KLAcc {
+    float m, se, A, C;
+};
+
+__device__ __forceinline__ KLAcc kl_empty() { return KLAcc{-INFINITY, 0.0f, 0.0f, 0.0f}; }
+
+// One visible entry with finite score s and target weight a >= 0.
+__device__ __forceinline__ void kl_add(KLAcc &k, float s, float a)
+{
+    const float mn = fmaxf(k.m, s);
+    k.se = k.se * __expf(k.m - mn) + __expf(s - mn);
+    k.m = mn;
+    k.A += a;
+    k.C += a > 0.0f ? a * (__logf(a) - s) : 0.0f;
+}
+
+__device__ __forceinline__ KLAcc kl_merge(const KLAcc &x, const KLAcc &y)
+{
+    const float mn = fmaxf(x.m, y.m);
+    KLAcc r;
+    r.m = mn;
+    r.se = (mn == -INFINITY) ? 0.0f : x.se * __expf(x.m - mn) + y.se * __expf(y.m - mn);
+    r.A = x.A + y.A;
+    r.C = x.C + y.C;
+    return r;
+}
+
+// Butterfly combine over the 64 lanes (every lane ends with the total).
+__device__ __forceinline__ KLAcc kl_wave_reduce(KLAcc k)
+{
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        KLAcc o;
+        o.m = __shfl_xor(k.m, off, kWave);
+        o.se = __shfl_xor(k.se, off, kWave);
+        o.A = __shfl_xor(k.A, off, kWave);
+        o.C = __shfl_xor(k.C, off, kWave);
+        // both partners combine (lower lane's statistics first) to the same bits
+        k = (lane() & off) ? kl_merge(o, k) : kl_merge(k, o);
+    }
+    return k;
+}
+
+// The divergence from a row's totals: 0 without a visible entry or target mass.
+__device__ __forceinline__ float kl_value(const KLAcc &k)
+{
+    if (k.m == -INFINITY || !(k.A > 0.0f))
+        return 0.0f;
+    return k.C / k.A + (k.m + __logf(k.se)) - __logf(k.A);
+}
+
+// ---------------------------------------------------------------------------
 // Row-tile plan.  A workgroup owns kRowsPerBlock consecutive query rows of one
 // batch row (one row per wave) and walks the compressed keys in tiles of
 // kTileEntries entries, double-buffered in LDS and shared by its waves (one
@@ -98,6 +157,10 @@ __device__ __forceinline__ float tile_scores(const RowOperand<HB, KS> &row, bool
 // mode & kModeScores: every score of the rows is written (masked = -inf).
 // mode & kModeSelect: each wave streams its row's scores through a TopKRow
 //                     candidate buffer in LDS and writes the row's top-k.
+// mode & kModeKL:     each wave folds its row's scores and target weights
+//                     into KL statistics (KLAcc) and writes the row's
+//                     divergence; the target of a tile is loaded one tile
+//                     ahead of its use.
 // ---------------------------------------------------------------------------
 // Up to 64 heads a row's operands leave room for two waves per
 // SIMD (at most 256 VGPRs), so one wave's MFMA work hides the other's
@@ -195,7 +258,15 @@ void rows_kernel(const KernelArgs a)
         if (kFullOps < G::kDmaPerWave && extra_op)
             dma16(r, dst + kFullOps * kRowWaves * kWave * 16, dma_off[G::kDmaPerWave - 1]);
     };
-    auto emit = [&](int tt, float s, bool valid) {
+    KLAcc klacc = kl_empty();
+    const float *tgt_row = (MODE & kModeKL) && active ? a.target + row_id * a.W : nullptr;
+    // this lane's target weight of tile tt (any value for entries past W)
+    auto tgt_load = [&](int tt) -> float {
+        if (!(MODE & kModeKL) || !active)
+            return 0.0f;
+        return tgt_row[min(tt * kTileEntries + l, a.W - 1)];
+    };
+    auto emit = [&](int tt, float s, bool valid, float tgt) {
         const int j = tt * kTileEntries + l;
         const float outv = valid ? s : -INFINITY;
         if (MODE & kModeScores) {
@@ -204,6 +275,10 @@ void rows_kernel(const KernelArgs a)
         }
         if (MODE & kModeSelect)
             topk_push(tk, score_key(outv), (uint32_t)j, valid);
+        if (MODE & kModeKL) {
+            if (valid)
+                kl_add(klacc, s, tgt);
+        }
     };
     auto tile_valid = [&](int tt) {
         const int j = tt * kTileEntries + l;
@@ -233,7 +308,7 @@ void rows_kernel(const KernelArgs a)
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
             c1[hb] = f32x16{};
-        float p0 = 0.0f;
+        float p0 = 0.0f, tgt_prev = 0.0f;
         bool prev_valid = false;
         for (int t = t_lo; t < ntiles; ++t) {
             wait_vm();
@@ -243,6 +318,9 @@ void rows_kernel(const KernelArgs a)
             if (active) {
                 const uint16_t *tile = ktile + (t & 1) * G::kTileElems;
                 const bool valid = tile_valid(t);
+                // tile t's target weights, used when its scores are emitted
+                // in the next iteration
+                const float tgt_cur = tgt_load(t);
                 float p1;
                 {
                     bf16x8 bf[KS];
@@ -259,14 +337,16 @@ void rows_kernel(const KernelArgs a)
                     load_entries_lds<KS>(bf, tile, 32, G::kPitch);
                     p0 = logits_with_partial<HB, KS>(c1, row, bf, c0, [&] {
                         if (t > t_lo)
-                            emit(t - 1, prev_score, prev_valid);
+                            emit(t - 1, prev_score, prev_valid, tgt_prev);
                     });
                 }
                 prev_valid = valid;
+                tgt_prev = tgt_cur;
             }
         }
         if (active && ntiles > t_lo)
-            emit(ntiles - 1, scaled_score(combine_halves(p0, logits_partial<HB, KS>(row, c1)), a.scale), prev_valid);
+            emit(ntiles - 1, scaled_score(combine_halves(p0, logits_partial<HB, KS>(row, c1)), a.scale), prev_valid,
+                 tgt_prev);
     } else {
         for (int t = t_lo; t < ntiles; ++t) {
             wait_vm();
@@ -276,10 +356,11 @@ void rows_kernel(const KernelArgs a)
             if (active) {
                 const uint16_t *tile = ktile + (t & 1) * G::kTileElems;
                 const bool valid = tile_valid(t);
+                const float tgt_cur = tgt_load(t);
                 const float s = tile_scores<HB, KS>(row, true, true, a.scale, [&](bf16x8(&bf)[KS], int sub) {
                     load_entries_lds<KS>(bf, tile, sub * 32, G::kPitch);
                 });
-                emit(t, s, valid);
+                emit(t, s, valid, tgt_cur);
             }
         }
     }
@@ -301,6 +382,11 @@ void rows_kernel(const KernelArgs a)
             topk_finish_regs<24>(tk, a.idx + row_id * a.top_k);
         else
             topk_finish(tk, a.idx + row_id * a.top_k);
+    }
+    if (MODE & kModeKL) {
+        const KLAcc tot = kl_wave_reduce(klacc);
+        if (l == 0)
+            a.kl[row_id] = kl_value(tot);
     }
 }
 
@@ -872,6 +958,47 @@ __global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(con
 }
 
 // ---------------------------------------------------------------------------
+// KL divergence and its gradient from a dense score matrix: one workgroup per
+// row.  Pass 1 folds the row's visible entries (finite scores; masked ones
+// are -inf) into KL statistics, pass 2 overwrites each score with
+// d kl / d score = exp(s - lse) - a / A (0 where masked, or when the row has
+// no visible entry or no target mass).
+// ---------------------------------------------------------------------------
+constexpr int kKLGradWaves = 4;
+
+__global__ __launch_bounds__(kKLGradWaves * kWave) void kl_grad_kernel(const KernelArgs a)
+{
+    __shared__ KLAcc part[kKLGradWaves];
+    const int64_t row = blockIdx.x;
+    const int wv = uniform(threadIdx.x / kWave);
+    float *s = a.scores + row * a.W;
+    const float *t = a.target + row * a.W;
+    KLAcc acc = kl_empty();
+    for (int j = threadIdx.x; j < a.W; j += kKLGradWaves * kWave) {
+        const float sv = s[j];
+        if (sv != -INFINITY)
+            kl_add(acc, sv, t[j]);
+    }
+    acc = kl_wave_reduce(acc);
+    if (lane() == 0)
+        part[wv] = acc;
+    __syncthreads();
+    KLAcc tot = part[0];
+#pragma unroll
+    for (int w = 1; w < kKLGradWaves; ++w)
+        tot = kl_merge(tot, part[w]);
+    if (threadIdx.x == 0)
+        a.kl[row] = kl_value(tot);
+    const bool has = tot.m != -INFINITY && tot.A > 0.0f;
+    const float lse = has ? tot.m + __logf(tot.se) : 0.0f;
+    const float inv_a = has ? 1.0f / tot.A : 0.0f;
+    for (int j = threadIdx.x; j < a.W; j += kKLGradWaves * kWave) {
+        const float sv = s[j];
+        s[j] = (has && sv != -INFINITY) ? __expf(sv - lse) - t[j] * inv_a : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers.
 // ---------------------------------------------------------------------------
 size_t rows_lds_bytes(int D, int mode, int cap)
@@ -912,6 +1039,8 @@ static hipError_t launch_rows_t(int mode, const KernelArgs &a, size_t lds, hipSt
         return launch(rows_kernel<D, HB, kModeSelect>, grid, block, lds, s, a);
     case kModeScores | kModeSelect:
         return launch(rows_kernel<D, HB, kModeScores | kModeSelect>, grid, block, lds, s, a);
+    case kModeKL:
+        return launch(rows_kernel<D, HB, kModeKL>, grid, block, lds, s, a);
     default:
         return hipErrorInvalidValue;
     }
@@ -996,6 +1125,12 @@ hipError_t launch_topk_block(const KernelArgs &a, size_t lds, hipStream_t s)
 {
     dim3 grid((unsigned)a.rows), block(kTopkBlockWaves * kWave);
     return launch(topk_block_kernel, grid, block, lds, s, a);
+}
+
+hipError_t launch_kl_grad(const KernelArgs &a, hipStream_t s)
+{
+    dim3 grid((unsigned)a.rows), block(kKLGradWaves * kWave);
+    return launch(kl_grad_kernel, grid, block, 0, s, a);
 }
 
 } // namespace csa

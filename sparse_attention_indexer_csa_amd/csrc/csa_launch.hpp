@@ -17,6 +17,8 @@ struct KernelArgs {
     const int32_t *k_seg;
     float *scores;   // [rows, W] (rows = B*S), dense
     int32_t *idx;    // [rows, top_k]
+    const float *target; // KL mode: [rows, W] target weights (>= 0), dense
+    float *kl;           // KL mode: [rows] divergence of each row
     int64_t q_sb, q_sh, q_ss;
     int64_t k_sb, k_sw;
     int64_t w_sb, w_ss;
@@ -47,7 +49,7 @@ constexpr int kTopkBlockWaves = 8;
 // Rows at least this long use the workgroup-per-row top-k.
 constexpr int kTopkBlockMinLen = 8192;
 
-enum { kModeScores = 1, kModeSelect = 2 };
+enum { kModeScores = 1, kModeSelect = 2, kModeKL = 4 };
 
 // Candidate-buffer capacity of the streaming top-k for a given k (room for at
 // least one more 64-pair push after a compaction down to k).  The row-tile
@@ -72,5 +74,9 @@ hipError_t launch_split(int D, int HB, const KernelArgs &a, hipStream_t s);
 hipError_t launch_stream(int D, int HB, const KernelArgs &a, int blocks, hipStream_t s);
 hipError_t launch_topk(const KernelArgs &a, size_t lds, hipStream_t s);
 hipError_t launch_topk_block(const KernelArgs &a, size_t lds, hipStream_t s);
+// KL divergence and its gradient from a dense score matrix held in a.scores
+// (-inf where masked): a.kl gets each row's divergence, a.scores is
+// overwritten with d kl / d score.
+hipError_t launch_kl_grad(const KernelArgs &a, hipStream_t s);
 
 } // namespace csa

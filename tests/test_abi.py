@@ -284,3 +284,27 @@ def test_noalloc_refuses_oversized_workspace_on_the_host(lib):
     assert lib.csa_index_select_noalloc(None, f, f, f, ctypes.byref(m), 16, f, None, None) == INVALID
     assert lib.csa_index_select_noalloc(ctypes.byref(prob()), f, f, f, ctypes.byref(m), 0, f, None, None) \
         == UNSUPPORTED
+
+
+def test_kl_loss_validation(lib):
+    """The loss checks its pointers on the host; an empty problem succeeds
+    without a launch."""
+    m = masks()
+    v = lambda x: ctypes.c_void_p(x) if x else None
+
+    def call(q=FAKE, k=FAKE, w=FAKE, t=FAKE, kl=FAKE, g=0, pp=None):
+        pp = pp or prob()
+        return lib.csa_index_kl_loss(ctypes.byref(pp), v(q), v(k), v(w), ctypes.byref(m), v(t), v(kl), v(g), None)
+
+    assert lib.csa_index_kl_loss(None, v(FAKE), v(FAKE), v(FAKE), ctypes.byref(m), v(FAKE), v(FAKE), None,
+                                 None) == INVALID
+    assert call(kl=0) == INVALID
+    assert call(kl=FAKE + 2) == INVALID
+    assert call(t=0) == INVALID
+    assert call(t=FAKE + 1) == INVALID
+    assert call(g=FAKE + 2) == INVALID
+    assert call(q=0) == INVALID
+    assert call(pp=prob(D=48)) == UNSUPPORTED
+    assert call(pp=prob(S=0), kl=0) == OK
+    # the plan field is ignored: a forced row-tile plan beyond its W limit is fine here
+    assert call(pp=prob(W=70000, plan=1), kl=0) == INVALID  # still needs kl
