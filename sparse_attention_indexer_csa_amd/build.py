@@ -1,4 +1,5 @@
-"""Builds libcsa_index.so (the HIP kernels + the C ABI) in place, for gfx950.
+"""Builds libcsa_index.so (the HIP kernels + the C ABI) and libcsa_calib.so
+(the benchmark's calibration kernels) in place, for gfx950.
 
     python -m sparse_attention_indexer_csa_amd.build
 
@@ -21,6 +22,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcsa_index.so")
 
 SOURCES = ["csa_kernels.hip", "csa_backward.hip", "csa_api.cpp"]
+# Calibration kernels for the benchmark's achievable peaks (include/csa_calib.h).
+CALIB_DIR = os.path.join(HERE, "calib")
+CALIB_SOURCE = "csa_calib.hip"
+CALIB_LIB = os.path.join(HERE, "libcsa_calib.so")
 HEADERS = ["csa_device.hpp", "csa_score.hpp", "csa_topk.hpp", "csa_launch.hpp", "csa_backward.hpp"]
 
 ARCH = os.environ.get("CSA_INDEX_ARCH", "gfx950")
@@ -57,18 +62,22 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the library (always, every source in parallel) and return its path."""
+    """Compile the library and the calibration library (always, every source
+    in parallel) and return the library's path."""
     tag = f".tmp{os.getpid()}"
     objs = [os.path.join(CSRC, s + tag + ".o") for s in SOURCES]
-    tmp = LIB + tag
+    calib_obj = os.path.join(CALIB_DIR, CALIB_SOURCE + tag + ".o")
+    jobs = [(os.path.join(CSRC, s), o) for s, o in zip(SOURCES, objs)]
+    jobs.append((os.path.join(CALIB_DIR, CALIB_SOURCE), calib_obj))
+    outs = [(LIB, objs), (CALIB_LIB, [calib_obj])]
     try:
-        with ThreadPoolExecutor(len(SOURCES)) as ex:
-            list(ex.map(lambda so: _run([hipcc(), *FLAGS, "-c", os.path.join(CSRC, so[0]), "-o", so[1]], verbose),
-                        zip(SOURCES, objs)))
-        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-        os.replace(tmp, LIB)
+        with ThreadPoolExecutor(len(jobs)) as ex:
+            list(ex.map(lambda so: _run([hipcc(), *FLAGS, "-c", so[0], "-o", so[1]], verbose), jobs))
+        for lib, lib_objs in outs:
+            _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *lib_objs, "-o", lib + tag], verbose)
+            os.replace(lib + tag, lib)
     finally:
-        for o in objs:
+        for o in objs + [calib_obj] + [lib + tag for lib, _ in outs]:
             if os.path.exists(o):
                 os.remove(o)
     return LIB

@@ -391,7 +391,7 @@ csa_status csa_index_score(const csa_index_problem *p, const void *q, const void
         a.full_rows = 1;
         return launched(csa::launch_split(p->D, c.HB, a, s), "split score");
     }
-    size_t lds = csa::rows_lds_bytes(p->D, csa::kModeScores, 0);
+    size_t lds = csa::rows_lds_bytes(p->D, c.HB, csa::kModeScores, 0);
     return launched(csa::launch_rows(p->D, c.HB, csa::kModeScores, a, lds, s), "row-tile score");
 }
 
@@ -485,8 +485,8 @@ csa_status csa_index_select(const csa_index_problem *p, const void *q, const voi
     }
 
     const int mode = csa::kModeSelect | (scores ? csa::kModeScores : 0);
-    a.cap = csa::rows_topk_capacity(top_k);
-    size_t lds = csa::rows_lds_bytes(p->D, mode, a.cap);
+    a.cap = csa::rows_topk_capacity(top_k, c.HB);
+    size_t lds = csa::rows_lds_bytes(p->D, c.HB, mode, a.cap);
     if ((st = device_lds_limit(lds, "row-tile select")) != CSA_OK)
         return st;
     a.scores = scores;
@@ -548,7 +548,7 @@ csa_status csa_index_kl_loss(const csa_index_problem *p, const void *q, const vo
     a.kl = kl;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!grad) {
-        const size_t lds = csa::rows_lds_bytes(pa.D, csa::kModeKL, 0);
+        const size_t lds = csa::rows_lds_bytes(pa.D, c.HB, csa::kModeKL, 0);
         if ((st = device_lds_limit(lds, "row-tile loss")) != CSA_OK)
             return st;
         return launched(csa::launch_rows(pa.D, c.HB, csa::kModeKL, a, lds, s), "row-tile loss");

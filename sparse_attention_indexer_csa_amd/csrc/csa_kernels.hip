@@ -162,20 +162,14 @@ __device__ __forceinline__ float kl_value(const KLAcc &k)
 //                     divergence; the target of a tile is loaded one tile
 //                     ahead of its use.
 // ---------------------------------------------------------------------------
-// Up to 64 heads a row's operands leave room for two waves per
-// SIMD (at most 256 VGPRs), so one wave's MFMA work hides the other's
-// epilogue and top-k bookkeeping; wider rows run one wave per SIMD.
-template <int D, int HB>
-constexpr int rows_waves_per_eu() { return HB <= 2 ? 2 : 1; }
-
+// This kernel serves rows of more than 64 heads (four head blocks), one wave
+// per SIMD; up to 64 heads rows3_kernel below takes the plan.
 template <int D, int HB, int MODE>
-__global__ __launch_bounds__(kRowWaves * kWave) __attribute__((amdgpu_waves_per_eu(rows_waves_per_eu<D, HB>())))
+__global__ __launch_bounds__(kRowWaves * kWave) __attribute__((amdgpu_waves_per_eu(1)))
 void rows_kernel(const KernelArgs a)
 {
     using G = TileGeom<D>;
     constexpr int KS = G::kKs;
-    // up to 64 heads the pipelined loop fits the register file
-    constexpr bool PIPE = HB <= 2;
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t *ktile = reinterpret_cast<uint16_t *>(smem);
 
@@ -227,7 +221,7 @@ void rows_kernel(const KernelArgs a)
         unsigned char *base = smem + 2 * G::kTileBytes + (size_t)wv * rows_topk_wave_bytes(a.cap);
         uint32_t *hist = reinterpret_cast<uint32_t *>(base);
         uint32_t *key = hist + 256;
-        topk_init(tk, key, reinterpret_cast<uint16_t *>(key + a.cap), hist, a.cap, a.top_k);
+        topk_init(tk, key, reinterpret_cast<uint16_t *>(key + a.cap + kWave), hist, a.cap, a.top_k);
     }
 
     // Key tiles arrive by DMA (no registers, no address arithmetic per tile):
@@ -274,7 +268,7 @@ void rows_kernel(const KernelArgs a)
                 a.scores[row_id * a.W + j] = outv;
         }
         if (MODE & kModeSelect)
-            topk_push(tk, score_key(outv), (uint32_t)j, valid);
+            topk_push_unchecked(tk, score_key(outv), (uint32_t)j, valid);
         if (MODE & kModeKL) {
             if (valid)
                 kl_add(klacc, s, tgt);
@@ -298,70 +292,21 @@ void rows_kernel(const KernelArgs a)
     if (active)
         load_row<HB, KS>(row, a.q + b * a.q_sb + (int64_t)i * a.q_ss, a.q_sh, a.w + b * a.w_sb + (int64_t)i * a.w_ss,
                          a.H);
-    if (PIPE) {
-        // Software pipeline over tiles: the MFMAs of subtile 0 of tile t run
-        // alongside the epilogue of subtile 1 of tile t-1, and the MFMAs of
-        // subtile 1 alongside the epilogue of subtile 0.  Tile t-1's scores
-        // are emitted between the two halves.  The body has no data-dependent
-        // branch, so each half is one scheduling region.
-        f32x16 c0[HB], c1[HB];
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-            c1[hb] = f32x16{};
-        float p0 = 0.0f, tgt_prev = 0.0f;
-        bool prev_valid = false;
-        for (int t = t_lo; t < ntiles; ++t) {
-            wait_vm();
-            __syncthreads();
-            if (t + 1 < ntiles)
-                fetch(t + 1);
-            if (active) {
-                const uint16_t *tile = ktile + (t & 1) * G::kTileElems;
-                const bool valid = tile_valid(t);
-                // tile t's target weights, used when its scores are emitted
-                // in the next iteration
-                const float tgt_cur = tgt_load(t);
-                float p1;
-                {
-                    bf16x8 bf[KS];
-                    load_entries_lds<KS>(bf, tile, 0, G::kPitch);
-                    p1 = logits_with_partial<HB, KS>(c0, row, bf, c1, [] {});
-                }
-                // combined unconditionally (a lane swap), so the epilogue
-                // above stays in the MFMA region instead of sinking into the
-                // branch; tile t-1's scores are emitted while the next
-                // subtile's first MFMAs run
-                const float prev_score = scaled_score(combine_halves(p0, p1), a.scale);
-                {
-                    bf16x8 bf[KS];
-                    load_entries_lds<KS>(bf, tile, 32, G::kPitch);
-                    p0 = logits_with_partial<HB, KS>(c1, row, bf, c0, [&] {
-                        if (t > t_lo)
-                            emit(t - 1, prev_score, prev_valid, tgt_prev);
-                    });
-                }
-                prev_valid = valid;
-                tgt_prev = tgt_cur;
-            }
-        }
-        if (active && ntiles > t_lo)
-            emit(ntiles - 1, scaled_score(combine_halves(p0, logits_partial<HB, KS>(row, c1)), a.scale), prev_valid,
-                 tgt_prev);
-    } else {
-        for (int t = t_lo; t < ntiles; ++t) {
-            wait_vm();
-            __syncthreads();
-            if (t + 1 < ntiles)
-                fetch(t + 1);
-            if (active) {
-                const uint16_t *tile = ktile + (t & 1) * G::kTileElems;
-                const bool valid = tile_valid(t);
-                const float tgt_cur = tgt_load(t);
-                const float s = tile_scores<HB, KS>(row, true, true, a.scale, [&](bf16x8(&bf)[KS], int sub) {
-                    load_entries_lds<KS>(bf, tile, sub * 32, G::kPitch);
-                });
-                emit(t, s, valid, tgt_cur);
-            }
+    for (int t = t_lo; t < ntiles; ++t) {
+        wait_vm();
+        __syncthreads();
+        if (t + 1 < ntiles)
+            fetch(t + 1);
+        if (active) {
+            const uint16_t *tile = ktile + (t & 1) * G::kTileElems;
+            const bool valid = tile_valid(t);
+            const float tgt_cur = tgt_load(t);
+            const float s = tile_scores<HB, KS>(row, true, true, a.scale, [&](bf16x8(&bf)[KS], int sub) {
+                load_entries_lds<KS>(bf, tile, sub * 32, G::kPitch);
+            });
+            if (MODE & kModeSelect)
+                topk_reserve(tk);
+            emit(t, s, valid, tgt_cur);
         }
     }
     if (active && (MODE & kModeScores)) {
@@ -378,6 +323,219 @@ void rows_kernel(const KernelArgs a)
     }
     if (MODE & kModeSelect) {
         // buffers of up to 1536 pairs (k <= 512) finish from registers
+        if (a.cap <= 24 * kWave)
+            topk_finish_regs<24>(tk, a.idx + row_id * a.top_k);
+        else
+            topk_finish(tk, a.idx + row_id * a.top_k);
+    }
+    if (MODE & kModeKL) {
+        const KLAcc tot = kl_wave_reduce(klacc);
+        if (l == 0)
+            a.kl[row_id] = kl_value(tot);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row-tile plan for up to 64 heads: three workgroups per compute unit (three
+// waves per SIMD), so that while one wave is in its epilogue, its top-k
+// bookkeeping or the final selection, two others keep the matrix core busy.
+// That budget (at most 168 VGPRs, 53 KB of LDS per workgroup) shapes the
+// loop: key tiles of 32 entries (double-buffered, one barrier per tile), the
+// B fragments of a tile read from LDS three k-steps ahead of their MFMAs
+// instead of all at once, one accumulator set per wave (the ReLU·w epilogue
+// of a tile follows its MFMAs; the other waves fill the matrix core
+// meanwhile), and a candidate buffer of k + 704 pairs.  Pairs of tiles make
+// the 64-entry units whose scores are pushed, written or folded (one score
+// per lane); segment skipping works on those units.  Everything else --
+// operands, masks, the order of operations, hence the bits -- is that of
+// rows_kernel.
+// ---------------------------------------------------------------------------
+constexpr int kTile3 = 32;
+
+template <int D>
+struct Tile3Geom {
+    static constexpr int kKs = D / 16;
+    static constexpr int kPitch = D + 8;                            // LDS row pitch (elements)
+    static constexpr int kRowChunks = kPitch / 8;                   // 16-byte slots per row
+    static constexpr int kDmaOps = (kTile3 * kRowChunks + kWave - 1) / kWave;
+    static constexpr int kDmaPerWave = (kDmaOps + kRowWaves - 1) / kRowWaves;
+    static constexpr size_t kBufBytes = (size_t)kDmaOps * kWave * 16; // whole DMA instructions
+};
+
+template <int D, int HB, int MODE>
+__global__ __launch_bounds__(kRowWaves * kWave) __attribute__((amdgpu_waves_per_eu(3)))
+void rows3_kernel(const KernelArgs a)
+{
+    using G = Tile3Geom<D>;
+    constexpr int KS = G::kKs;
+    static_assert(HB <= 2, "three waves per SIMD hold at most two head blocks");
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int tid = threadIdx.x;
+    const int wv = uniform(tid / kWave);
+    const int l = lane();
+
+    const int rb = a.n_row_blocks - 1 - (int)(blockIdx.x / a.B);
+    const int b = (int)(blockIdx.x % a.B);
+    const int row0 = rb * kRowsPerBlock;
+    const int i = row0 + wv;
+    const bool active = i < a.S;
+
+    const int64_t off = a.q_offset ? (int64_t)a.q_offset[b] : 0;
+    const int last = min(row0 + kRowsPerBlock, a.S) - 1;
+    const int thr_last = visible_entries(off + last, a.m, a.W);
+    const int nunits = (thr_last + kTileEntries - 1) / kTileEntries; // 64-entry units
+    const int ntiles = (thr_last + kTile3 - 1) / kTile3;             // 32-entry tiles
+    const int thr = active ? visible_entries(off + i, a.m, a.W) : 0;
+    const int qseg = (a.q_seg && active) ? a.q_seg[(int64_t)b * a.S + i] : 0;
+    const int32_t *kseg = a.k_seg ? a.k_seg + (int64_t)b * a.W : nullptr;
+    const int64_t row_id = (int64_t)b * a.S + i;
+
+    // With segments, units before the first one that holds an entry of any
+    // row's segment are masked for the whole workgroup and are skipped.
+    int u_lo = 0;
+    if (kseg) {
+        __shared__ int first_unit[kRowWaves];
+        int fu = nunits;
+        if (active) {
+            for (int u = 0; u < nunits; ++u) {
+                const int j = u * kTileEntries + l;
+                if (ballot(j < thr && kseg[min(j, a.W - 1)] == qseg) != 0ull) {
+                    fu = u;
+                    break;
+                }
+            }
+        }
+        if (l == 0)
+            first_unit[wv] = fu;
+        __syncthreads();
+#pragma unroll
+        for (int w2 = 0; w2 < kRowWaves; ++w2)
+            u_lo = w2 == 0 ? first_unit[0] : min(u_lo, first_unit[w2]);
+    }
+
+    TopKRow<uint16_t> tk;
+    if (MODE & kModeSelect) {
+        unsigned char *base = smem + 2 * G::kBufBytes + (size_t)wv * rows_topk_wave_bytes(a.cap);
+        uint32_t *hist = reinterpret_cast<uint32_t *>(base);
+        uint32_t *key = hist + 256;
+        topk_init(tk, key, reinterpret_cast<uint16_t *>(key + a.cap + kWave), hist, a.cap, a.top_k);
+    }
+
+    // Key tiles by DMA, as in rows_kernel: DMA instruction o of a tile writes
+    // the 64 16-byte slots 64o .. 64o+63 of the padded image; slots past the
+    // tile's entries (and past W) read zeros and are never consumed.
+    const uint16_t *kb = a.k + b * a.k_sb;
+    const int entry_bytes = (int)a.k_sw * 2;
+    const int64_t tile_stride = (int64_t)kTile3 * a.k_sw;
+    const int W = a.W;
+    uint32_t dma_off[G::kDmaPerWave];
+#pragma unroll
+    for (int x = 0; x < G::kDmaPerWave; ++x) {
+        const int slot = (wv + x * kRowWaves) * kWave + l;
+        dma_off[x] = (uint32_t)((slot / G::kRowChunks) * entry_bytes + (slot % G::kRowChunks) * 16);
+    }
+    auto fetch = [&](int t) {
+        const int n = min(W - t * kTile3, kTile3);
+        const __amdgpu_buffer_rsrc_t r = raw_rsrc(kb + t * tile_stride, entries_span<D>(n, entry_bytes));
+        unsigned char *dst = smem + (size_t)(t & 1) * G::kBufBytes + wv * kWave * 16;
+#pragma unroll
+        for (int x = 0; x < G::kDmaPerWave; ++x)
+            if (wv + x * kRowWaves < G::kDmaOps)
+                dma16(r, dst + x * kRowWaves * kWave * 16, dma_off[x]);
+    };
+
+    KLAcc klacc = kl_empty();
+    const float *tgt_row = (MODE & kModeKL) && active ? a.target + row_id * a.W : nullptr;
+    auto tgt_load = [&](int u) -> float {
+        if (!(MODE & kModeKL) || !active)
+            return 0.0f;
+        return tgt_row[min(u * kTileEntries + l, a.W - 1)];
+    };
+    auto unit_valid = [&](int u) {
+        const int j = u * kTileEntries + l;
+        bool v = j < thr;
+        if (kseg)
+            v = v && kseg[min(j, a.W - 1)] == qseg;
+        return v;
+    };
+    auto emit = [&](int u, float s, bool valid, float tgt) {
+        const int j = u * kTileEntries + l;
+        const float outv = valid ? s : -INFINITY;
+        if (MODE & kModeScores) {
+            if (j < a.W)
+                a.scores[row_id * a.W + j] = outv;
+        }
+        if (MODE & kModeSelect)
+            topk_push_unchecked(tk, score_key(outv), (uint32_t)j, valid);
+        if (MODE & kModeKL) {
+            if (valid)
+                kl_add(klacc, s, tgt);
+        }
+    };
+
+    const int t_lo = 2 * u_lo;
+    if (ntiles > t_lo)
+        fetch(t_lo);
+    RowOperand<HB, KS> row;
+    if (active)
+        load_row<HB, KS>(row, a.q + b * a.q_sb + (int64_t)i * a.q_ss, a.q_sh, a.w + b * a.w_sb + (int64_t)i * a.w_ss,
+                         a.H);
+    // this lane's B fragment of k-step s: entry (l % 32), values 16s + 8(l / 32)
+    const int boff = (l & 31) * G::kPitch + 8 * (l >> 5);
+    float p_even = 0.0f, tgt_unit = 0.0f;
+    for (int t = t_lo; t < ntiles; ++t) {
+        wait_vm();
+        __syncthreads();
+        if (t + 1 < ntiles)
+            fetch(t + 1);
+        if (active) {
+            const uint16_t *tile = reinterpret_cast<const uint16_t *>(smem + (size_t)(t & 1) * G::kBufBytes);
+            if ((t & 1) == 0)
+                tgt_unit = tgt_load(t >> 1);
+            f32x16 c[HB];
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+                c[hb] = f32x16{};
+            constexpr int kAhead = KS < 3 ? KS : 3;
+            bf16x8 bq[kAhead];
+#pragma unroll
+            for (int s2 = 0; s2 < kAhead; ++s2)
+                bq[s2] = load_frag(tile + boff + 16 * s2);
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2) {
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb)
+                    c[hb] = mfma32(row.a[hb][s2], bq[s2 % kAhead], c[hb]);
+                if (s2 + kAhead < KS)
+                    bq[s2 % kAhead] = load_frag(tile + boff + 16 * (s2 + kAhead));
+            }
+            const float p = logits_partial<HB, KS>(row, c);
+            if ((t & 1) == 0 && t + 1 < ntiles) {
+                p_even = p;
+            } else {
+                // a 64-entry unit is complete: entries of the odd tile (or
+                // none past an even last tile) sit in the upper lane half
+                const int u = t >> 1;
+                const bool odd = (t & 1) != 0;
+                const float sc = scaled_score(combine_halves(odd ? p_even : p, odd ? p : 0.0f), a.scale);
+                const bool valid = unit_valid(u);
+                if (MODE & kModeSelect)
+                    topk_reserve(tk);
+                emit(u, sc, valid, tgt_unit);
+            }
+        }
+    }
+    if (!active)
+        return;
+    if (MODE & kModeScores) {
+        // entries before the first computed unit and past the last are masked
+        for (int j = l; j < min(u_lo * kTileEntries, a.W); j += kWave)
+            a.scores[row_id * a.W + j] = -INFINITY;
+        for (int j = max(nunits, u_lo) * kTileEntries + l; j < a.W; j += kWave)
+            a.scores[row_id * a.W + j] = -INFINITY;
+    }
+    if (MODE & kModeSelect) {
         if (a.cap <= 24 * kWave)
             topk_finish_regs<24>(tk, a.idx + row_id * a.top_k);
         else
@@ -1001,9 +1159,18 @@ __global__ __launch_bounds__(kKLGradWaves * kWave) void kl_grad_kernel(const Ker
 // ---------------------------------------------------------------------------
 // Host-side launchers.
 // ---------------------------------------------------------------------------
-size_t rows_lds_bytes(int D, int mode, int cap)
+size_t rows_lds_bytes(int D, int HB, int mode, int cap)
 {
-    size_t tile = 2 * (size_t)kTileEntries * (D + 8) * 2;
+    size_t tile;
+    if (HB <= 2) {
+        switch (D) {
+        case 32: tile = 2 * Tile3Geom<32>::kBufBytes; break;
+        case 64: tile = 2 * Tile3Geom<64>::kBufBytes; break;
+        default: tile = 2 * Tile3Geom<128>::kBufBytes; break;
+        }
+    } else {
+        tile = 2 * (size_t)kTileEntries * (D + 8) * 2;
+    }
     size_t sel = (mode & kModeSelect) ? (size_t)kRowWaves * rows_topk_wave_bytes(cap) : 0;
     return tile + sel;
 }
@@ -1032,17 +1199,32 @@ template <int D, int HB>
 static hipError_t launch_rows_t(int mode, const KernelArgs &a, size_t lds, hipStream_t s)
 {
     dim3 grid((unsigned)((int64_t)a.B * a.n_row_blocks)), block(kRowWaves * kWave);
-    switch (mode) {
-    case kModeScores:
-        return launch(rows_kernel<D, HB, kModeScores>, grid, block, lds, s, a);
-    case kModeSelect:
-        return launch(rows_kernel<D, HB, kModeSelect>, grid, block, lds, s, a);
-    case kModeScores | kModeSelect:
-        return launch(rows_kernel<D, HB, kModeScores | kModeSelect>, grid, block, lds, s, a);
-    case kModeKL:
-        return launch(rows_kernel<D, HB, kModeKL>, grid, block, lds, s, a);
-    default:
-        return hipErrorInvalidValue;
+    if constexpr (HB <= 2) {
+        switch (mode) {
+        case kModeScores:
+            return launch(rows3_kernel<D, HB, kModeScores>, grid, block, lds, s, a);
+        case kModeSelect:
+            return launch(rows3_kernel<D, HB, kModeSelect>, grid, block, lds, s, a);
+        case kModeScores | kModeSelect:
+            return launch(rows3_kernel<D, HB, kModeScores | kModeSelect>, grid, block, lds, s, a);
+        case kModeKL:
+            return launch(rows3_kernel<D, HB, kModeKL>, grid, block, lds, s, a);
+        default:
+            return hipErrorInvalidValue;
+        }
+    } else {
+        switch (mode) {
+        case kModeScores:
+            return launch(rows_kernel<D, HB, kModeScores>, grid, block, lds, s, a);
+        case kModeSelect:
+            return launch(rows_kernel<D, HB, kModeSelect>, grid, block, lds, s, a);
+        case kModeScores | kModeSelect:
+            return launch(rows_kernel<D, HB, kModeScores | kModeSelect>, grid, block, lds, s, a);
+        case kModeKL:
+            return launch(rows_kernel<D, HB, kModeKL>, grid, block, lds, s, a);
+        default:
+            return hipErrorInvalidValue;
+        }
     }
 }
 

@@ -56,13 +56,20 @@ enum { kModeScores = 1, kModeSelect = 2, kModeKL = 4 };
 // kernel stores 16-bit entries and affords a larger buffer, so most rows never
 // compact mid-stream.
 __host__ __device__ constexpr int topk_capacity(int k) { return ((k + 63) / 64) * 64 + 512; }
-__host__ __device__ constexpr int rows_topk_capacity(int k) { return ((k + 63) / 64) * 64 + 1024; }
-// LDS bytes of one wave's row-tile buffer: histogram, keys, 16-bit entries.
-__host__ __device__ constexpr size_t rows_topk_wave_bytes(int cap) { return 1024 + (size_t)cap * 6; }
+// With up to two head blocks the row-tile kernel runs three workgroups per
+// compute unit and its buffers are smaller.
+__host__ __device__ constexpr int rows_topk_capacity(int k, int HB)
+{
+    return ((k + 63) / 64) * 64 + (HB <= 2 ? 704 : 1024);
+}
+// LDS bytes of one wave's row-tile buffer: histogram, keys, 16-bit entries,
+// each array with 64 slots past cap for the lanes of a push whose pairs do
+// not enter (topk_push_unchecked).
+__host__ __device__ constexpr size_t rows_topk_wave_bytes(int cap) { return 1024 + (size_t)(cap + 64) * 6; }
 // Entries of the row-tile plan are stored in 16 bits.
 constexpr int kRowTilesMaxW = 65536;
 
-size_t rows_lds_bytes(int D, int mode, int cap);
+size_t rows_lds_bytes(int D, int HB, int mode, int cap);
 size_t topk_lds_bytes(int cap);
 size_t topk_block_lds_bytes(int cap, int top_k);
 

@@ -180,49 +180,6 @@ __device__ __forceinline__ float subtile_partial(const RowOperand<HB, KS> &r, co
     return logits_partial<HB, KS>(r, c);
 }
 
-// Logits of one subtile (into cnew, from zero) and the partial of another
-// subtile whose logits are cold, interleaved in program order: every k-step
-// issues one MFMA per head block (independent accumulators, so no MFMA waits
-// on the previous one) followed by its share of the cold subtile's
-// max + fma work, which runs while the matrix core is busy.  Scheduling
-// fences keep that order.  The fma chains visit heads in the same order as
-// logits_partial(), so the partial is bit-identical to it.
-template <int HB, int KS, typename Mid>
-__device__ __forceinline__ float logits_with_partial(f32x16 (&cnew)[HB], const RowOperand<HB, KS> &r,
-                                                     const bf16x8 (&b)[KS], const f32x16 (&cold)[HB], Mid mid)
-{
-    static_assert((HB * 16) % KS == 0, "epilogue must split evenly over the k-steps");
-    constexpr int kPer = HB * 16 / KS;
-    float acc[HB];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-        cnew[hb] = f32x16{};
-        acc[hb] = 0.0f;
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-            cnew[hb] = mfma32(r.a[hb][s], b[s], cnew[hb]);
-        // work handed in by the caller runs while the first k-step's MFMAs
-        // are in the pipe
-        if (s == 0)
-            mid();
-#pragma unroll
-        for (int p = 0; p < kPer; ++p) {
-            const int idx = s * kPer + p, hb = idx / 16, rr = idx % 16;
-            acc[hb] = __builtin_fmaf(r.w[hb][rr], relu(cold[hb][rr]), acc[hb]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int step = 1; step < HB; step <<= 1)
-#pragma unroll
-        for (int hb = 0; hb + step < HB; hb += 2 * step)
-            acc[hb] += acc[hb + step];
-    return acc[0];
-}
-
 // Combine the lane shares of two 32-entry subtiles (entries j0..j0+31 in p0,
 // j0+32..j0+63 in p1): after one swap of lane halves, lane l holds the full
 // unscaled score of entry j0 + l (its own half's share plus the other half's,

@@ -325,6 +325,29 @@ __device__ __forceinline__ void topk_push(TopKRow<EntT> &t, uint32_t kv, uint32_
     t.count += n;
 }
 
+// The push without a capacity check or branch, for code that keeps
+// count + 64 <= cap itself (topk_reserve): lanes whose pair does not enter
+// write it to their own slot past the buffer (cap + lane), which the buffer
+// must provide (64 slots beyond cap in both arrays).
+template <typename EntT>
+__device__ __forceinline__ void topk_push_unchecked(TopKRow<EntT> &t, uint32_t kv, uint32_t entry, bool valid)
+{
+    const bool pass = valid && kv > t.tau;
+    const uint64_t bal = ballot(pass);
+    const int pos = pass ? t.count + rank_below(bal) : t.cap + lane();
+    t.key[pos] = kv;
+    t.ent[pos] = (EntT)entry;
+    t.count += popc64(bal);
+}
+
+// Room for one more push of 64 pairs.
+template <typename EntT>
+__device__ __forceinline__ void topk_reserve(TopKRow<EntT> &t)
+{
+    if (t.count + kWave > t.cap)
+        topk_make_room(t);
+}
+
 // ---------------------------------------------------------------------------
 // Bitonic sort of 64*E values held by one wave, lane l holding elements
 // l*E .. l*E+E-1, into descending order.  Partners in other lanes come from
