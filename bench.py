@@ -8,33 +8,43 @@ Inputs are resident in HBM before timing starts; the selection output is
 int32 [S, 512] and the score matrix never reaches HBM.
 
 value = causal score entries per second = (unmasked (i, j) pairs) / step time.
-Also reported on the same line:
+Also reported on the same line (each leg: HIP events around every call on
+the launch stream, mean / median / min over the timed calls):
   roofline      the fused kernel's algorithmic flops (pairs * 2*H*D) per launch
-                over its mean HIP-event duration, against the dense bf16 MFMA peak
+                over its mean event duration, against the dense bf16 MFMA peak,
+                and against the achievable MFMA rate measured in this run
+  achievable    calibration kernels on the same GPU: a back-to-back bf16 MFMA
+                loop on Gaussian and on zero operands (the chip lowers its clock
+                under the higher switching power of Gaussian data), a streaming
+                read and a copy of 1 GiB
   scores_only   csa_index_score on the same workload (fp32 [S,W] output)
+  packed        the packed-document prefill (B=4, S=8192, W=2048, 1-6 documents
+                per row, segment + causal mask), fused select
   decode        B=64 one-row decode over a 32768-entry cache (valid length
                 U[4096,32768]): rows/s and HBM fraction of the algorithmic bytes
-  backward      csa_index_score_backward on the same workload (dq, dk, dw for a
+  backward      csa_index_score_backward on the prefill workload (dq, dk, dw for a
                 Gaussian upstream gradient): algorithmic flops pairs * 6*H*D
-                (logit recompute, dq and dk products) over the call's duration
-  cpu_baseline  the CPU oracle (scores + top-k) on a bounded sample of the rows
-  copy          (leg "copy", off by default) a plain 1 GiB device copy, the
-                calibration kernel for the FETCH_SIZE / WRITE_SIZE counters
+  kl            csa_index_kl_loss on the prefill workload (fused, no gradient):
+                the indexer's KL loss against a random target distribution
+  cpu_baseline  the CPU oracle (scores + top-k) on a bounded sample of the
+                prefill rows, and of the decode rows
 
 Every leg first runs its step untimed for --settle-s seconds (default 0.5)
 so that the GPU's clocks have ramped up under the load before the W warmup
 and K timed steps; without it the first few dozen calls of a leg run up to
 25 % slower and a short run times the ramp.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--settle-s S]
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--settle-s S] [--legs ...]
 """
 
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -47,20 +57,17 @@ METRIC = "indexer score entries/sec (causal) + % bf16 MFMA peak; decode rows/sec
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 CSRC = os.path.join(ROOT, "sparse_attention_indexer_csa_amd", "csrc")
+CALIB_LIB = os.path.join(ROOT, "sparse_attention_indexer_csa_amd", "libcsa_calib.so")
 
 # HBM bytes per launch of the fused prefill kernel, from FETCH_SIZE and
 # WRITE_SIZE counter runs scaled by what the same counters read for a plain
 # copy of known size.  Valid only for the kernel sources they were taken on
 # (sha256 over the files the forward kernels are compiled from); reported as
 # null otherwise.
-MEASURED_TRAFFIC = {
-    "sources_sha": "fe00158dc0c145c04f73acd6e783eddb5b354a88a76bea612039acaa31286e6a",
-    # FETCH_SIZE 139986.3 KiB x 1.99995 (copy calibration) + WRITE_SIZE 32768 KiB x 1.0
-    "bytes_per_launch": 320_239_000,
-}
-
+MEASURED_TRAFFIC = None
 
 FORWARD_SOURCES = ["csa_device.hpp", "csa_kernels.hip", "csa_launch.hpp", "csa_score.hpp", "csa_topk.hpp"]
+DEFAULT_LEGS = "calib,select,score,packed,decode,backward,kl,cpu"
 
 
 def sources_sha():
@@ -80,7 +87,7 @@ def measured_traffic():
 
 def row_kernel_name(P):
     hb = 1 if P.H <= 32 else 2 if P.H <= 64 else 4
-    return f"csa::rows_kernel<{P.D}, {hb}, 2>"
+    return f"csa::rows3_kernel<{P.D}, {hb}, 2>" if hb <= 2 else f"csa::rows_kernel<{P.D}, {hb}, 2>"
 
 
 def log(*a):
@@ -92,9 +99,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="select,score,decode,backward,cpu",
-                    help="comma list of: select, score, decode, backward, cpu, copy")
-    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+    ap.add_argument("--legs", default=DEFAULT_LEGS,
+                    help="comma list of: calib, select, score, packed, decode, backward, kl, cpu")
+    ap.add_argument("--settle-s", type=float, default=0.5,
                     help="untimed seconds of calls before each leg's warmup (clock ramp); 0 disables")
     ap.add_argument("--cpu-row-stride", type=int, default=2,
                     help="the CPU baseline runs every n-th row of the prefill workload")
@@ -114,14 +121,14 @@ def to_device(P, dev):
                 k_seg=i32(P.k_seg))
 
 
-def visible_pairs(P, rows=None):
+def visible_pairs(P, rows=None, segments=True):
     """Unmasked (row, entry) pairs: entries before the causal threshold (and in
-    the row's segment when segments are given)."""
+    the row's segment when segments are given and counted)."""
     rows = np.arange(P.B * P.S) if rows is None else np.asarray(rows)
     b, i = rows // P.S, rows % P.S
     off = P.q_offset[b].astype(np.int64) if P.q_offset is not None else 0
     thr = np.clip((off + i + 1) // P.m, 0, P.W)
-    if P.q_seg is None:
+    if P.q_seg is None or not segments:
         return int(thr.sum())
     total = 0
     for bb in np.unique(b):
@@ -142,8 +149,9 @@ def time_calls(fn, steps, warmup, torch):
     """Runs fn untimed for SETTLE_S seconds of wall time (the GPU raises its
     clocks over the first tens of milliseconds under load, so a short warmup
     would time the ramp instead of the steady state), then warmup more untimed
-    calls, then steps timed calls; returns (wall ms per step, mean event ms
-    per call)."""
+    calls, then steps timed calls, each between two HIP events on the current
+    stream (the stream the binding launches on).  Returns wall ms per step and
+    the mean, median and min event ms per call."""
     t_end = time.perf_counter() + SETTLE_S
     while time.perf_counter() < t_end:
         for _ in range(8):
@@ -160,8 +168,77 @@ def time_calls(fn, steps, warmup, torch):
         evs[s][1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    ev = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    return wall, ev
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    return dict(wall_ms=wall, ev_mean=float(ms.mean()), ev_median=float(np.median(ms)), ev_min=float(ms.min()))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def calibrate(torch, dev, steps, warmup):
+    """Achievable rates on this GPU from the calibration kernels."""
+    lib = ctypes.CDLL(CALIB_LIB)
+    lib.csa_calib_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p]
+    lib.csa_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                                   ctypes.c_void_p]
+    lib.csa_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                   ctypes.c_void_p]
+    for f in (lib.csa_calib_mfma_bf16, lib.csa_calib_read, lib.csa_calib_copy):
+        f.restype = ctypes.c_int32
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = lambda: ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    out = {}
+    # operands: Gaussian values scaled like the indexer's q and k, as bf16
+    rng = np.random.default_rng(0)
+    g = (rng.standard_normal(256 * 8).astype(np.float32) / np.float32(np.sqrt(128.0)))
+    bits = ((g.view(np.uint32) + np.uint32(0x7FFF) + ((g.view(np.uint32) >> 16) & 1)) >> 16).astype(np.uint16)
+    ops = {"gauss": torch.from_numpy(bits.view(np.int16)).to(dev),
+           "zeros": torch.zeros(256 * 8, dtype=torch.int16, device=dev)}
+    blocks, iters = 8 * cus, 2000
+    sink = torch.empty(blocks * 4, dtype=torch.float32, device=dev)
+    flops = blocks * 4 * iters * 8 * 32768
+    for name, o in ops.items():
+        def step(_, o=o):
+            st = lib.csa_calib_mfma_bf16(ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(sink.data_ptr()), blocks,
+                                         iters, stream())
+            if st != 0:
+                raise RuntimeError(f"calibration MFMA launch failed ({st})")
+        t = time_calls(step, max(3, steps // 4), warmup, torch)
+        out[f"mfma_bf16_tflops_{name}"] = flops / (t["ev_median"] * 1e-3) / 1e12
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    rsink = torch.empty(8 * cus * 256, dtype=torch.int32, device=dev)
+
+    def step_r(_):
+        if lib.csa_calib_read(ctypes.c_void_p(src.data_ptr()), n, ctypes.c_void_p(rsink.data_ptr()), 8 * cus,
+                              stream()) != 0:
+            raise RuntimeError("calibration read launch failed")
+
+    def step_c(_):
+        if lib.csa_calib_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n, 8 * cus,
+                              stream()) != 0:
+            raise RuntimeError("calibration copy launch failed")
+
+    t = time_calls(step_r, max(3, steps // 4), warmup, torch)
+    out["hbm_read_GBs"] = n / (t["ev_median"] * 1e-3) / 1e9
+    t = time_calls(step_c, max(3, steps // 4), warmup, torch)
+    out["hbm_copy_GBs"] = 2 * n / (t["ev_median"] * 1e-3) / 1e9
+    out["copy_bytes_read"] = n
+    out["copy_bytes_written"] = n
+    out["note"] = ("MFMA loop: 8 workgroups of 4 waves per CU, back-to-back v_mfma_f32_32x32x16_bf16 on 4 "
+                   "accumulators; read/copy: 1 GiB, 16-byte accesses, 8 workgroups per CU; median event time")
+    del src, dst
+    return out
 
 
 def main():
@@ -198,20 +275,32 @@ def main():
                    "plan": csa.resolve_plan(d["q"], d["k"], d["w"], P.m)},
     }
 
+    achievable = None
+    if "calib" in legs:
+        log("calibration legs (MFMA loop, read, copy)")
+        achievable = calibrate(torch, dev, args.steps, args.warmup)
+        result["achievable"] = achievable
+
     if "select" in legs:
         def step(_):
             csa.select(d["q"], d["k"], d["w"], P.top_k, P.m, out=out_idx)
 
         log(f"select: {args.warmup} warmup + {args.steps} timed steps")
-        wall, ev = time_calls(step, args.steps, args.warmup, torch)
-        result["value"] = pairs / (wall * 1e-3)
-        result["ms_per_step"] = wall
-        achieved = flops / (ev * 1e-3) / 1e12
-        result["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                              "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
-                              "kernel": row_kernel_name(P), "kernel_ms": ev,
-                              "flops_per_launch": flops, "sources_sha": sources_sha()[:16]}
-        log(f"select: {wall:.3f} ms/step, kernel {ev:.3f} ms, {achieved:.1f} TFLOP/s")
+        t = time_calls(step, args.steps, args.warmup, torch)
+        result["value"] = pairs / (t["wall_ms"] * 1e-3)
+        result["ms_per_step"] = t["wall_ms"]
+        achieved = flops / (t["ev_mean"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                "kernel": row_kernel_name(P), "kernel_ms_mean": t["ev_mean"], "kernel_ms_median": t["ev_median"],
+                "kernel_ms_min": t["ev_min"], "flops_per_launch": flops, "sources_sha": sources_sha()[:16]}
+        if achievable:
+            ach = achievable["mfma_bf16_tflops_gauss"]
+            roof["achievable_peak"] = ach
+            roof["frac_of_achievable"] = achieved / ach
+        result["roofline"] = roof
+        log(f"select: {t['wall_ms']:.3f} ms/step, kernel mean {t['ev_mean']:.3f} median {t['ev_median']:.3f} "
+            f"min {t['ev_min']:.3f} ms, {achieved:.1f} TFLOP/s")
 
     if "score" in legs:
         out_s = torch.empty((P.B, P.S, P.W), dtype=torch.float32, device=dev)
@@ -220,12 +309,75 @@ def main():
             csa.score(d["q"], d["k"], d["w"], P.m, out=out_s)
 
         log("scores-only leg")
-        wall, ev = time_calls(step_s, args.steps, args.warmup, torch)
-        ach = flops / (ev * 1e-3) / 1e12
-        result["scores_only"] = {"entries_per_s": pairs / (wall * 1e-3), "ms_per_step": wall, "kernel_ms": ev,
-                                 "tflops": ach, "mfma_frac": ach / PEAK_BF16_TFLOPS,
+        t = time_calls(step_s, args.steps, args.warmup, torch)
+        ach = flops / (t["ev_mean"] * 1e-3) / 1e12
+        result["scores_only"] = {"entries_per_s": pairs / (t["wall_ms"] * 1e-3), "ms_per_step": t["wall_ms"],
+                                 "kernel_ms_mean": t["ev_mean"], "kernel_ms_median": t["ev_median"],
+                                 "kernel_ms_min": t["ev_min"], "tflops": ach, "mfma_frac": ach / PEAK_BF16_TFLOPS,
                                  "output": "fp32 [S,W] = %d MiB" % (P.S * P.W * 4 >> 20)}
         del out_s
+
+    if "kl" in legs:
+        gen = torch.Generator(device=dev).manual_seed(17)
+        target = torch.rand((P.B, P.S, P.W), generator=gen, device=dev, dtype=torch.float32)
+        kl_out = torch.empty((P.B, P.S), dtype=torch.float32, device=dev)
+
+        def step_kl(_):
+            csa.kl_loss(d["q"], d["k"], d["w"], target, P.m, out=kl_out)
+
+        log("kl leg")
+        t = time_calls(step_kl, args.steps, args.warmup, torch)
+        ach = flops / (t["ev_mean"] * 1e-3) / 1e12
+        result["kl"] = {"workload": "indexer KL loss, fused (no gradient), random target, " + CONFIG_TITLES["c3"],
+                        "entries_per_s": pairs / (t["wall_ms"] * 1e-3), "ms_per_step": t["wall_ms"],
+                        "kernel_ms_mean": t["ev_mean"], "kernel_ms_median": t["ev_median"],
+                        "kernel_ms_min": t["ev_min"], "tflops": ach, "mfma_frac": ach / PEAK_BF16_TFLOPS}
+        del target, kl_out
+
+    if "backward" in legs:
+        # gradient of sum(g * score) for a Gaussian upstream gradient g [B,S,W]
+        gen = torch.Generator(device=dev).manual_seed(13)
+        g = torch.randn((P.B, P.S, P.W), generator=gen, device=dev, dtype=torch.float32)
+        dq = torch.empty((P.B, P.H, P.S, P.D), dtype=torch.float32, device=dev)
+        dk = torch.empty((P.B, P.W, P.D), dtype=torch.float32, device=dev)
+        dw = torch.empty((P.B, P.S, P.H), dtype=torch.float32, device=dev)
+        wsb = torch.empty(csa.backward_workspace_size(d["q"], d["k"], d["w"], P.m), dtype=torch.uint8, device=dev)
+
+        def step_b(_):
+            csa.score_backward(d["q"], d["k"], d["w"], g, P.m, workspace=wsb, dq=dq, dk=dk, dw=dw)
+
+        log("backward leg")
+        t = time_calls(step_b, args.steps, args.warmup, torch)
+        bflops = pairs * 6 * P.H * P.D
+        ach = bflops / (t["ev_mean"] * 1e-3) / 1e12
+        result["backward"] = {"workload": "gradients dq, dk, dw of sum(g * score) on " + CONFIG_TITLES["c3"],
+                              "entries_per_s": pairs / (t["wall_ms"] * 1e-3), "ms_per_step": t["wall_ms"],
+                              "call_ms_mean": t["ev_mean"], "call_ms_median": t["ev_median"],
+                              "call_ms_min": t["ev_min"], "flops_per_call": bflops, "tflops": ach,
+                              "mfma_frac": ach / PEAK_BF16_TFLOPS, "workspace_bytes": wsb.numel()}
+        log(f"backward: {t['wall_ms']:.3f} ms/step, call {t['ev_mean']:.3f} ms, {ach:.1f} TFLOP/s")
+        del g, dq, dk, dw, wsb
+
+    del d
+    if "packed" in legs:
+        Pp = make_config("c4")
+        dp = to_device(Pp, dev)
+        seg_pairs = visible_pairs(Pp)
+        causal_pairs = visible_pairs(Pp, segments=False)
+        out_p = torch.empty((Pp.B, Pp.S, Pp.top_k), dtype=torch.int32, device=dev)
+
+        def step_p(_):
+            csa.select(dp["q"], dp["k"], dp["w"], Pp.top_k, Pp.m, q_seg=dp["q_seg"], k_seg=dp["k_seg"], out=out_p)
+
+        log("packed-document leg")
+        t = time_calls(step_p, args.steps, args.warmup, torch)
+        ach = seg_pairs * 2 * Pp.H * Pp.D / (t["ev_mean"] * 1e-3) / 1e12
+        result["packed"] = {"workload": CONFIG_TITLES["c4"] + ", fused select, seed 4",
+                            "entries_per_s": seg_pairs / (t["wall_ms"] * 1e-3), "ms_per_step": t["wall_ms"],
+                            "kernel_ms_mean": t["ev_mean"], "kernel_ms_median": t["ev_median"],
+                            "kernel_ms_min": t["ev_min"], "same_segment_pairs": seg_pairs,
+                            "causal_pairs": causal_pairs, "tflops": ach, "mfma_frac": ach / PEAK_BF16_TFLOPS}
+        del dp, out_p, Pp
 
     if "decode" in legs:
         Pd = make_config("c5")
@@ -244,63 +396,39 @@ def main():
                        workspace=ws)
 
         log("decode leg")
-        wall, ev = time_calls(step_d, args.steps, args.warmup, torch)
-        gbs = alg_bytes / (ev * 1e-3) / 1e9
-        result["decode"] = {"workload": CONFIG_TITLES["c5"], "rows_per_s": Pd.B / (wall * 1e-3),
-                            "ms_per_step": wall, "call_ms": ev, "algorithmic_bytes": alg_bytes, "GB_s": gbs,
-                            "hbm_frac": gbs / PEAK_HBM_GBS,
-                            "plan": csa.resolve_plan(dd["q"], dd["k"], dd["w"], Pd.m)}
+        t = time_calls(step_d, args.steps, args.warmup, torch)
+        gbs = alg_bytes / (t["ev_mean"] * 1e-3) / 1e9
+        dec = {"workload": CONFIG_TITLES["c5"], "rows_per_s": Pd.B / (t["wall_ms"] * 1e-3),
+               "ms_per_step": t["wall_ms"], "call_ms_mean": t["ev_mean"], "call_ms_median": t["ev_median"],
+               "call_ms_min": t["ev_min"], "algorithmic_bytes": alg_bytes, "GB_s": gbs,
+               "hbm_frac": gbs / PEAK_HBM_GBS, "plan": csa.resolve_plan(dd["q"], dd["k"], dd["w"], Pd.m)}
+        if achievable:
+            dec["hbm_frac_of_achievable_read"] = gbs / achievable["hbm_read_GBs"]
+        result["decode"] = dec
         del caches, dd, ws
-
-    if "backward" in legs:
-        # gradient of sum(g * score) for a Gaussian upstream gradient g [B,S,W]
-        gen = torch.Generator(device=dev).manual_seed(13)
-        g = torch.randn((P.B, P.S, P.W), generator=gen, device=dev, dtype=torch.float32)
-        dq = torch.empty((P.B, P.H, P.S, P.D), dtype=torch.float32, device=dev)
-        dk = torch.empty((P.B, P.W, P.D), dtype=torch.float32, device=dev)
-        dw = torch.empty((P.B, P.S, P.H), dtype=torch.float32, device=dev)
-        wsb = torch.empty(csa.backward_workspace_size(d["q"], d["k"], d["w"], P.m), dtype=torch.uint8, device=dev)
-
-        def step_b(_):
-            csa.score_backward(d["q"], d["k"], d["w"], g, P.m, workspace=wsb, dq=dq, dk=dk, dw=dw)
-
-        log("backward leg")
-        wall, ev = time_calls(step_b, args.steps, args.warmup, torch)
-        bflops = pairs * 6 * P.H * P.D
-        ach = bflops / (ev * 1e-3) / 1e12
-        result["backward"] = {"workload": "gradients dq, dk, dw of sum(g * score) on " + CONFIG_TITLES["c3"],
-                              "entries_per_s": pairs / (wall * 1e-3), "ms_per_step": wall, "call_ms": ev,
-                              "flops_per_call": bflops, "tflops": ach, "mfma_frac": ach / PEAK_BF16_TFLOPS,
-                              "workspace_bytes": wsb.numel()}
-        log(f"backward: {wall:.3f} ms/step, call {ev:.3f} ms, {ach:.1f} TFLOP/s")
-        del g, dq, dk, dw, wsb
-
-    if "copy" in legs:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-
-        def step_c(_):
-            dst.copy_(src)
-
-        log("copy leg")
-        wall, ev = time_calls(step_c, args.steps, args.warmup, torch)
-        result["copy"] = {"bytes_read": n, "bytes_written": n, "call_ms": ev, "GB_s": 2 * n / (ev * 1e-3) / 1e9}
-        del src, dst
 
     if "cpu" in legs:
         import oracle
 
+        cpu = {"unit": "entries/s", "cores": oracle.threads(), "host_cpus_visible": len(os.sched_getaffinity(0)),
+               "cpu_model": cpu_model(), "kind": "oracle"}
         rows = np.arange(0, P.S, args.cpu_row_stride)
         sample_pairs = visible_pairs(P, rows)
         log(f"cpu baseline: oracle on {len(rows)} rows ({sample_pairs} pairs), {oracle.threads()} threads")
         t0 = time.perf_counter()
         oracle.select(P, rows)
         dt = time.perf_counter() - t0
-        result["cpu_baseline"] = {"value": sample_pairs / dt, "unit": "entries/s", "cores": oracle.threads(),
-                                  "kind": "oracle", "seconds": dt,
-                                  "sample": f"every {args.cpu_row_stride}th query row of the seq-16384 prefill "
-                                            f"({len(rows)} rows, {sample_pairs} causal pairs), scores + top-k"}
+        cpu.update(value=sample_pairs / dt, seconds=dt,
+                   sample=f"every {args.cpu_row_stride}th query row of the seq-16384 prefill "
+                          f"({len(rows)} rows, {sample_pairs} causal pairs), scores + top-k")
+        Pd = make_config("c5")
+        drows = np.arange(0, Pd.B, 4)
+        t0 = time.perf_counter()
+        oracle.select(Pd, drows)
+        dtd = time.perf_counter() - t0
+        cpu["decode"] = {"rows_per_s": len(drows) / dtd, "seconds": dtd,
+                         "sample": f"every 4th decode row ({len(drows)} of {Pd.B}), scores + top-k"}
+        result["cpu_baseline"] = cpu
 
     print(json.dumps(result), flush=True)
 

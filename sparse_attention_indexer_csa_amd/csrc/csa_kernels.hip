@@ -64,6 +64,29 @@ __device__ __forceinline__ void vm_wait_le()
 
 __device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// First 64-entry unit u < nunits that holds an entry j < thr of segment qseg
+// (nunits if there is none).  The segment ids of eight units are loaded at
+// once, so a row whose segment starts late costs a few memory round trips,
+// not one per unit.
+__device__ __forceinline__ int first_segment_unit(const int32_t *kseg, int thr, int qseg, int nunits, int W)
+{
+    constexpr int kBatch = 8;
+    const int l = lane();
+    for (int u0 = 0; u0 < nunits; u0 += kBatch) {
+        int v[kBatch];
+#pragma unroll
+        for (int r = 0; r < kBatch; ++r)
+            v[r] = kseg[min((u0 + r) * kTileEntries + l, W - 1)];
+#pragma unroll
+        for (int r = 0; r < kBatch; ++r) {
+            const int j = (u0 + r) * kTileEntries + l;
+            if (u0 + r < nunits && ballot(j < thr && v[r] == qseg) != 0ull)
+                return u0 + r;
+        }
+    }
+    return nunits;
+}
+
 // Scores of the 64 entries j0 .. j0+63 of one row: lane l returns the
 // scaled score of entry j0 + l.  Subtiles (32 entries) flagged off are not
 // computed (their lanes return garbage that the caller masks).  `load(b, sub)`
@@ -197,16 +220,7 @@ void rows_kernel(const KernelArgs a)
     int t_lo = 0;
     if (kseg) {
         __shared__ int first_tile[kRowWaves];
-        int ft = ntiles;
-        if (active) {
-            for (int t = 0; t < ntiles; ++t) {
-                const int j = t * kTileEntries + l;
-                if (ballot(j < thr && kseg[min(j, a.W - 1)] == qseg) != 0ull) {
-                    ft = t;
-                    break;
-                }
-            }
-        }
+        const int ft = active ? first_segment_unit(kseg, thr, qseg, ntiles, a.W) : ntiles;
         if (l == 0)
             first_tile[wv] = ft;
         __syncthreads();
@@ -396,16 +410,7 @@ void rows3_kernel(const KernelArgs a)
     int u_lo = 0;
     if (kseg) {
         __shared__ int first_unit[kRowWaves];
-        int fu = nunits;
-        if (active) {
-            for (int u = 0; u < nunits; ++u) {
-                const int j = u * kTileEntries + l;
-                if (ballot(j < thr && kseg[min(j, a.W - 1)] == qseg) != 0ull) {
-                    fu = u;
-                    break;
-                }
-            }
-        }
+        const int fu = active ? first_segment_unit(kseg, thr, qseg, nunits, a.W) : nunits;
         if (l == 0)
             first_unit[wv] = fu;
         __syncthreads();
@@ -452,11 +457,14 @@ void rows3_kernel(const KernelArgs a)
             return 0.0f;
         return tgt_row[min(u * kTileEntries + l, a.W - 1)];
     };
-    auto unit_valid = [&](int u) {
+    // segment id of this lane's entry of unit u (loaded at the unit's first
+    // tile, compared at its last, so the load's latency is hidden)
+    auto seg_load = [&](int u) -> int { return kseg ? kseg[min(u * kTileEntries + l, a.W - 1)] : 0; };
+    auto unit_valid = [&](int u, int seg) {
         const int j = u * kTileEntries + l;
         bool v = j < thr;
         if (kseg)
-            v = v && kseg[min(j, a.W - 1)] == qseg;
+            v = v && seg == qseg;
         return v;
     };
     auto emit = [&](int u, float s, bool valid, float tgt) {
@@ -484,6 +492,7 @@ void rows3_kernel(const KernelArgs a)
     // this lane's B fragment of k-step s: entry (l % 32), values 16s + 8(l / 32)
     const int boff = (l & 31) * G::kPitch + 8 * (l >> 5);
     float p_even = 0.0f, tgt_unit = 0.0f;
+    int seg_unit = 0;
     for (int t = t_lo; t < ntiles; ++t) {
         wait_vm();
         __syncthreads();
@@ -491,8 +500,10 @@ void rows3_kernel(const KernelArgs a)
             fetch(t + 1);
         if (active) {
             const uint16_t *tile = reinterpret_cast<const uint16_t *>(smem + (size_t)(t & 1) * G::kBufBytes);
-            if ((t & 1) == 0)
+            if ((t & 1) == 0) {
                 tgt_unit = tgt_load(t >> 1);
+                seg_unit = seg_load(t >> 1);
+            }
             f32x16 c[HB];
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb)
@@ -519,7 +530,7 @@ void rows3_kernel(const KernelArgs a)
                 const int u = t >> 1;
                 const bool odd = (t & 1) != 0;
                 const float sc = scaled_score(combine_halves(odd ? p_even : p, odd ? p : 0.0f), a.scale);
-                const bool valid = unit_valid(u);
+                const bool valid = unit_valid(u, seg_unit);
                 if (MODE & kModeSelect)
                     topk_reserve(tk);
                 emit(u, sc, valid, tgt_unit);
