@@ -509,6 +509,44 @@ __device__ __forceinline__ uint32_t med3u(uint32_t a, uint32_t b, uint32_t c)
     return r;
 }
 
+// Compare-exchange of element r with the same element of lane l ^ LX for
+// LX = 16 or 32, two elements (r, r + 1) at a time: one lane swap between the
+// two registers leaves, in every lane, both values of one of the two pairs
+// (element r's pair in the lanes whose LX bit is clear, element r + 1's in
+// the others); both results are computed in that lane and a second swap puts
+// them back.  The lane holding a pair computes its own result into the
+// register of its own element, and its partner's into the other.
+template <int LX>
+__device__ __forceinline__ void swap_halves(uint32_t &x, uint32_t &y)
+{
+    static_assert(LX == 16 || LX == 32, "lane swaps exist for distances 16 and 32");
+    const auto sw = LX == 16 ? __builtin_amdgcn_permlane16_swap(x, y, false, false)
+                             : __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    x = sw[0];
+    y = sw[1];
+}
+
+template <int E, int LX>
+__device__ __forceinline__ void cross_stage32_swapped(uint32_t (&v)[E], uint32_t sel, int l)
+{
+    static_assert(E % 2 == 0, "elements are exchanged in pairs");
+    // in lanes whose LX bit is set the pair held is the partner's element
+    // r + 1 (first) and this lane's (second): the results trade places
+    const uint32_t s_first = (l & LX) ? ~sel : sel;
+#pragma unroll
+    for (int r = 0; r < E; r += 2)
+        swap_halves<LX>(v[r], v[r + 1]);
+#pragma unroll
+    for (int r = 0; r < E; r += 2) {
+        const uint32_t x = v[r], y = v[r + 1];
+        v[r] = med3u(x, y, s_first);
+        v[r + 1] = med3u(x, y, ~s_first);
+    }
+#pragma unroll
+    for (int r = 0; r < E; r += 2)
+        swap_halves<LX>(v[r], v[r + 1]);
+}
+
 template <int E, int SIZE, int STRIDE>
 __device__ __forceinline__ void bitonic32_cross_levels(uint32_t (&v)[E], int l)
 {
@@ -516,9 +554,20 @@ __device__ __forceinline__ void bitonic32_cross_levels(uint32_t (&v)[E], int l)
         const int e = l * E;
         const bool keep_max = ((e & STRIDE) == 0) == ((e & SIZE) == 0);
         const uint32_t sel = keep_max ? 0xFFFFFFFFu : 0u;
+        constexpr int LX = STRIDE / E;
+        if constexpr ((LX == 16 || LX == 32) && E % 2 == 0) {
+            cross_stage32_swapped<E, LX>(v, sel, l);
+        } else {
+            // all exchanges first, then the compare-exchanges, so no
+            // exchange waits on the result just computed
+            uint32_t o[E];
 #pragma unroll
-        for (int r = 0; r < E; ++r)
-            v[r] = med3u(v[r], lane_xor_u32<STRIDE / E>(v[r]), sel);
+            for (int r = 0; r < E; ++r)
+                o[r] = lane_xor_u32<LX>(v[r]);
+#pragma unroll
+            for (int r = 0; r < E; ++r)
+                v[r] = med3u(v[r], o[r], sel);
+        }
         bitonic32_cross_levels<E, SIZE, STRIDE / 2>(v, l);
     }
 }
