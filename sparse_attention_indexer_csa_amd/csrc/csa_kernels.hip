@@ -710,8 +710,12 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(const Kernel
 // ---------------------------------------------------------------------------
 constexpr int kStreamMaxRows = kStreamRows;
 
+// Two waves per SIMD: without the bound the compiler takes all 256 VGPRs and
+// some accumulation registers besides, which leaves one wave per SIMD and
+// half of the launched workgroups waiting for the other half.
 template <int D, int HB>
-__global__ __launch_bounds__(kSplitWaves * kWave) void stream_kernel(const KernelArgs a)
+__global__ __launch_bounds__(kSplitWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void stream_kernel(const KernelArgs a)
 {
     using G = SplitGeom<D>;
     constexpr int KS = D / 16;
