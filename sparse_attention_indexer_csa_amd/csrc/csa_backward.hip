@@ -15,7 +15,9 @@
 // contracted on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 //
 // Pass 1 (bwd_rows_kernel): a workgroup owns a few query rows, one wave per
-// (row, 32-head block); key tiles of 32 entries are staged in LDS and shared.
+// (row, 32-head block); key tiles of 64 entries are staged in LDS and shared;
+// the dq product reads its key operand down the tile's columns with
+// transposing LDS reads.
 // The transposed logits l[j, h] come out of the MFMA with one head per lane,
 // which is the layout the dq product needs for its A operand, so the
 // elementwise step stays in registers.  dw is a per-lane register sum.
@@ -57,15 +59,30 @@ __device__ __forceinline__ bf16x8 operand_from(const float (&v)[16], int base)
     return __builtin_bit_cast(bf16x8, u);
 }
 
-// Eight bf16 values gathered from LDS as one MFMA operand.
-__device__ __forceinline__ bf16x8 gather8(const uint16_t *p, const int (&off)[8])
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// An MFMA operand whose eight contraction values run down a column of a
+// row-major bf16 matrix in LDS (element (r, col) at r * pitch + col), read with
+// two transposing LDS reads.  Within each 16-lane group, ds_read_b64_tr_b16
+// hands lane i element i % 4 of the 8-byte pieces addressed by lanes
+// 4e + i / 4 (e = 0..3).  With the lane offset below, lane l of the wave
+// receives rows c_row(0..7, l / 32) = {4g..4g+3, 8+4g..8+4g+3} (g = l / 32) of
+// the 16-row block at `blk`, column l % 32 of the 32-column block: the k
+// layout of the operands produced from the 32x32 MFMA accumulators.
+__device__ __forceinline__ int tr_lane_offset(int pitch)
 {
-    u32x4 u;
-    u.x = (uint32_t)p[off[0]] | ((uint32_t)p[off[1]] << 16);
-    u.y = (uint32_t)p[off[2]] | ((uint32_t)p[off[3]] << 16);
-    u.z = (uint32_t)p[off[4]] | ((uint32_t)p[off[5]] << 16);
-    u.w = (uint32_t)p[off[6]] | ((uint32_t)p[off[7]] << 16);
-    return __builtin_bit_cast(bf16x8, u);
+    const int l = lane();
+    return (4 * (l >> 5) + ((l >> 2) & 3)) * pitch + 16 * ((l >> 4) & 1) + 4 * (l & 3);
+}
+
+__device__ __forceinline__ bf16x8 load_column_operand(const uint16_t *blk, int off, int pitch)
+{
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(blk + off));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(blk + off + 8 * pitch));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
 }
 
 __device__ __forceinline__ int64_t row_offset(const BwdArgs &a, int b)
@@ -93,16 +110,9 @@ constexpr int kRowTile = 64;
 template <int D>
 struct RowTileGeom {
     static constexpr int kPitch = D + 8;                  // LDS row pitch (elements)
-    static constexpr int kPitchT = kRowTile + 8;          // transposed tile: entries per column + pad
     static constexpr int kChunks = kRowTile * D / 8;      // 16-byte pieces per key tile
     static constexpr int kPerThread = (kChunks + kBwdThreads - 1) / kBwdThreads;
 };
-
-// Position of entry e (0..31) of a key tile in a column of the transposed
-// tile: bits 2 and 3 swapped, so the eight entries 16jb + c_row(0..7, g) that
-// one lane contracts in the dq product sit at 16jb + 8g + 0..7, one 16-byte
-// read.
-__device__ __forceinline__ int tposed(int e) { return (e & 0x13) | ((e & 4) << 1) | ((e & 8) >> 1); }
 
 template <int D, int HB>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_rows_kernel(const BwdArgs a)
@@ -110,10 +120,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     using G = RowTileGeom<D>;
     constexpr int KS = D / 16, DB = D / 32, P = G::kPitch;
     constexpr int RPW = kBwdWaves / HB; // query rows per workgroup
-    constexpr int PT = G::kPitchT;
-    // key tile, entry-major (logits) and column-major (dq product)
+    // key tile, entry-major: B operand of the logits by 16-byte reads, B
+    // operand of the dq product by transposing reads
     __shared__ __attribute__((aligned(16))) uint16_t tile[2][kRowTile * P];
-    __shared__ __attribute__((aligned(16))) uint16_t tileT[2][D * PT];
     // each row's upstream gradients of the tile, 0 where masked
     __shared__ __attribute__((aligned(16))) float gtile[2][RPW][kRowTile];
 
@@ -157,10 +166,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             acc[c][r] = 0.0f;
     float dw_acc = 0.0f;
 
+    // this lane's offset of the transposing reads of the key tile: entries
+    // c_row(0..7, gi) of a 16-entry block, column n (plus 32c columns)
+    const int ktr = tr_lane_offset(P);
     // Staging: piece c holds eight columns 8(c / kRowTile) .. +7 of entry
-    // c % kRowTile, so the lanes of a wave cover consecutive entries and their
-    // column-major stores fall in consecutive positions.  In the column-major
-    // copy, subtile h of the tile occupies positions 32h .. 32h+31.
+    // c % kRowTile, so the lanes of a wave cover consecutive entries.
     uint4 pre[G::kPerThread];
     auto fetch = [&](int t) {
 #pragma unroll
@@ -178,16 +188,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         for (int u = 0; u < G::kPerThread; ++u) {
             const int c = tid + u * kBwdThreads;
             const int row = c % kRowTile, col = (c / kRowTile) * 8;
-            if (c < G::kChunks) {
+            if (c < G::kChunks)
                 *reinterpret_cast<uint4 *>(&tile[buf][row * P + col]) = pre[u];
-                uint16_t *dst = &tileT[buf][col * PT + (row & ~31) + tposed(row & 31)];
-                const uint32_t v[4] = {pre[u].x, pre[u].y, pre[u].z, pre[u].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    dst[(2 * e) * PT] = (uint16_t)v[e];
-                    dst[(2 * e + 1) * PT] = (uint16_t)(v[e] >> 16);
-                }
-            }
         }
     };
 
@@ -257,11 +259,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 pf[r] = x > 0.0f ? ge[r] : 0.0f; // rounded to bf16 by operand_from
             }
             const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
-            const uint16_t *TT = tileT[t & 1] + n * PT + 32 * hs + 8 * gi;
+            // B operand: entries 32hs + c_row(0..7, gi) (+16), column 32c + n
+            const uint16_t *Tk = tile[t & 1] + 32 * hs * P;
 #pragma unroll
             for (int c = 0; c < DB; ++c) {
-                acc[c] = mfma32(a0, load_frag(TT + 32 * c * PT), acc[c]);
-                acc[c] = mfma32(a1, load_frag(TT + 32 * c * PT + 16), acc[c]);
+                acc[c] = mfma32(a0, load_column_operand(Tk + 32 * c, ktr, P), acc[c]);
+                acc[c] = mfma32(a1, load_column_operand(Tk + 16 * P + 32 * c, ktr, P), acc[c]);
             }
         }
         }
@@ -354,14 +357,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     }
     const int kseg = a.k_seg ? a.k_seg[(int64_t)b * a.W + min(j, a.W - 1)] : 0;
 
-    // LDS offsets of this lane's transposed q reads: head 16kb + c_row(e, gi),
-    // column n (plus 32hb heads and 32c columns).
-    int qoff[2][8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            qoff[kb][e] = (16 * kb + c_row(e, gi)) * P + n;
+    // this lane's offset of the transposing reads of the q block: heads
+    // 16kb + c_row(0..7, gi), column n (plus 32hb heads and 32c columns)
+    const int qtr = tr_lane_offset(P);
 
     f32x16 acc[DB];
 #pragma unroll
@@ -449,8 +447,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 const uint16_t *Qh = Q + 32 * hb * P;
 #pragma unroll
                 for (int c = 0; c < DB; ++c) {
-                    acc[c] = mfma32(a0, gather8(Qh + 32 * c, qoff[0]), acc[c]);
-                    acc[c] = mfma32(a1, gather8(Qh + 32 * c, qoff[1]), acc[c]);
+                    acc[c] = mfma32(a0, load_column_operand(Qh + 32 * c, qtr, P), acc[c]);
+                    acc[c] = mfma32(a1, load_column_operand(Qh + 32 * c + 16 * P, qtr, P), acc[c]);
                 }
             }
         }
