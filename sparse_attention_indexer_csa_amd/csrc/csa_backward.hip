@@ -61,25 +61,80 @@ __device__ __forceinline__ bf16x8 operand_from(const float (&v)[16], int base)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// An MFMA operand whose eight contraction values run down a column of a
-// row-major bf16 matrix in LDS (element (r, col) at r * pitch + col), read with
-// two transposing LDS reads.  Within each 16-lane group, ds_read_b64_tr_b16
-// hands lane i element i % 4 of the 8-byte pieces addressed by lanes
-// 4e + i / 4 (e = 0..3).  With the lane offset below, lane l of the wave
-// receives rows c_row(0..7, l / 32) = {4g..4g+3, 8+4g..8+4g+3} (g = l / 32) of
-// the 16-row block at `blk`, column l % 32 of the 32-column block: the k
-// layout of the operands produced from the 32x32 MFMA accumulators.
-__device__ __forceinline__ int tr_lane_offset(int pitch)
+// Key tiles and q blocks sit in LDS row-major with D bf16 columns and no
+// padding.  The 16-byte chunk c of row r is stored at chunk c ^ swizzle(r) of
+// that row, so that with 64 four-byte banks neither access pattern conflicts:
+// 16 lanes reading 16 consecutive rows at one chunk (row operands, staging
+// stores), and a transposing read, whose 32 lanes read four consecutive rows
+// at four consecutive chunks.  The swizzle uses bits 0-3 of the row only, and
+// moving 8 rows down flips its bit 1.
+template <int D>
+__device__ __forceinline__ int swizzle(int r)
 {
-    const int l = lane();
-    return (4 * (l >> 5) + ((l >> 2) & 3)) * pitch + 16 * ((l >> 4) & 1) + 4 * (l & 3);
+    static_assert(D == 32 || D == 64 || D == 128, "tile widths 32, 64, 128");
+    if constexpr (D == 128)
+        return 4 * (r & 3) + ((r >> 2) & 3);
+    else if constexpr (D == 64)
+        return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    else
+        return (r >> 2) & 3;
 }
 
-__device__ __forceinline__ bf16x8 load_column_operand(const uint16_t *blk, int off, int pitch)
+// element offset of chunk c (columns 8c .. 8c+7) of row r
+template <int D>
+__device__ __forceinline__ int tile_offset(int r, int c)
+{
+    return r * D + 8 * (c ^ swizzle<D>(r));
+}
+
+// This lane's row operand addressing: row r (the lane's entry or head) at
+// chunk 2s + gi (the eight values of k-step s) is at row_base + 8 * (2s ^ x).
+struct RowLane {
+    int row_base, x;
+};
+
+template <int D>
+__device__ __forceinline__ RowLane row_lane(int r, int gi)
+{
+    return {r * D, gi ^ swizzle<D>(r)};
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 load_row_operand(const uint16_t *tile, const RowLane &rl, int s)
+{
+    return load_frag(tile + rl.row_base + 8 * ((2 * s) ^ rl.x));
+}
+
+// An MFMA operand whose eight contraction values run down a column of a
+// swizzled tile, read with two transposing LDS reads.  Within each 16-lane
+// group, ds_read_b64_tr_b16 hands lane i element i % 4 of the 8-byte pieces
+// addressed by lanes 4e + i / 4 (e = 0..3).  Lane l addresses row
+// 4(l / 32) + (l / 4) % 4 of the block, columns 16((l / 16) % 2) + 4(l % 4) ..
+// +3, and so receives rows c_row(0..7, l / 32) = {4g..4g+3, 8+4g..8+4g+3}
+// (g = l / 32) of the 16-row block, column l % 32 of the 32-column block: the
+// k layout of the operands produced from the 32x32 MFMA accumulators.
+struct ColLane {
+    int base, y;
+};
+
+template <int D>
+__device__ __forceinline__ ColLane col_lane()
+{
+    const int l = lane();
+    const int r = 4 * (l >> 5) + ((l >> 2) & 3);
+    const int c = 2 * ((l >> 4) & 1) + ((l >> 1) & 1);
+    return {r * D + 4 * (l & 1), c ^ swizzle<D>(r)};
+}
+
+// rows r0 .. r0+15 (r0 a multiple of 16), columns 32cb .. 32cb+31
+template <int D>
+__device__ __forceinline__ bf16x8 load_column_operand(const uint16_t *tile, const ColLane &cl, int r0, int cb)
 {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(blk + off));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(blk + off + 8 * pitch));
+    const uint16_t *lo_p = tile + r0 * D + cl.base + 8 * ((4 * cb) ^ cl.y);
+    const uint16_t *hi_p = tile + (r0 + 8) * D + cl.base + 8 * ((4 * cb) ^ cl.y ^ 2);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)lo_p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)hi_p);
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
@@ -109,7 +164,6 @@ constexpr int kRowTile = 64;
 
 template <int D>
 struct RowTileGeom {
-    static constexpr int kPitch = D + 8;                  // LDS row pitch (elements)
     static constexpr int kChunks = kRowTile * D / 8;      // 16-byte pieces per key tile
     static constexpr int kPerThread = (kChunks + kBwdThreads - 1) / kBwdThreads;
 };
@@ -118,11 +172,11 @@ template <int D, int HB>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_rows_kernel(const BwdArgs a)
 {
     using G = RowTileGeom<D>;
-    constexpr int KS = D / 16, DB = D / 32, P = G::kPitch;
+    constexpr int KS = D / 16, DB = D / 32;
     constexpr int RPW = kBwdWaves / HB; // query rows per workgroup
-    // key tile, entry-major: B operand of the logits by 16-byte reads, B
-    // operand of the dq product by transposing reads
-    __shared__ __attribute__((aligned(16))) uint16_t tile[2][kRowTile * P];
+    // key tile, entry-major and swizzled: A operand of the logits by 16-byte
+    // reads, B operand of the dq product by transposing reads
+    __shared__ __attribute__((aligned(16))) uint16_t tile[2][kRowTile * D];
     // each row's upstream gradients of the tile, 0 where masked
     __shared__ __attribute__((aligned(16))) float gtile[2][RPW][kRowTile];
 
@@ -166,9 +220,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             acc[c][r] = 0.0f;
     float dw_acc = 0.0f;
 
-    // this lane's offset of the transposing reads of the key tile: entries
-    // c_row(0..7, gi) of a 16-entry block, column n (plus 32c columns)
-    const int ktr = tr_lane_offset(P);
+    // this lane's addressing of the key tile: entry n of a 32-entry subtile
+    // (logits), entries c_row(0..7, gi) of a 16-entry block, column n (dq)
+    const RowLane krow = row_lane<D>(n, gi);
+    const ColLane kcol = col_lane<D>();
     // Staging: piece c holds eight columns 8(c / kRowTile) .. +7 of entry
     // c % kRowTile, so the lanes of a wave cover consecutive entries.
     uint4 pre[G::kPerThread];
@@ -189,31 +244,36 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             const int c = tid + u * kBwdThreads;
             const int row = c % kRowTile, col = (c / kRowTile) * 8;
             if (c < G::kChunks)
-                *reinterpret_cast<uint4 *>(&tile[buf][row * P + col]) = pre[u];
+                *reinterpret_cast<uint4 *>(&tile[buf][tile_offset<D>(row, col / 8)]) = pre[u];
         }
     };
 
     // The masked gradients of a row's tile are loaded once, by the row's
     // first head-block wave (one entry per lane), and staged in LDS with the
-    // key tile.
+    // key tile.  The loaded values are masked only when they are stored, after
+    // the tile's products: using them earlier would make the wave wait for the
+    // loads before its matrix work.
     static_assert(kRowTile == kWave, "one gradient per lane");
     const int wr = wv / HB; // this wave's row within the workgroup
     const bool g_lane = hb == 0;
-    float gnext = 0.0f;
+    float gnext = 0.0f; // gradient of this lane's next entry, as loaded
+    int snext = 0;      // its segment id, as loaded
+    bool gvis = false;  // whether the entry is before the row's threshold
     auto fetch_g = [&](int t) {
         if (g_lane && active) {
             const int j = kRowTile * t + l;
             const int jc = min(j, a.W - 1);
-            bool ok = j < thr;
+            gvis = j < thr;
             if (a.k_seg)
-                ok = ok && a.k_seg[(int64_t)b * a.W + jc] == qseg;
-            const float gv = grow[jc];
-            gnext = ok ? gv : 0.0f;
+                snext = a.k_seg[(int64_t)b * a.W + jc];
+            gnext = grow[jc];
         }
     };
     auto store_g = [&](int buf) {
-        if (g_lane)
-            gtile[buf][wr][l] = gnext;
+        if (g_lane) {
+            const bool ok = gvis && (!a.k_seg || snext == qseg);
+            gtile[buf][wr][l] = ok ? gnext : 0.0f;
+        }
     };
 
     if (ntiles > 0) {
@@ -222,6 +282,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         store(0);
         store_g(0);
     }
+    // Every load issued so far (the q operands included) completes here, so
+    // that inside the loop only the next tile's loads are in flight and the
+    // products never wait for them.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
         if (t + 1 < ntiles) {
@@ -231,7 +295,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
         for (int hs = 0; hs < kRowTile / 32; ++hs) {
         if (active && kRowTile * t + 32 * hs < thr) {
-            const uint16_t *T = tile[t & 1] + 32 * hs * P;
+            const uint16_t *T = tile[t & 1] + 32 * hs * D;
             // upstream gradient of this lane's 16 entries c_row(r, gi)
             float ge[16];
             const float *gt = gtile[t & 1][wr] + 32 * hs;
@@ -250,7 +314,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 lt[r] = 0.0f;
 #pragma unroll
             for (int s = 0; s < KS; ++s)
-                lt = mfma32(load_frag(T + n * P + 16 * s + 8 * gi), qf[s], lt);
+                lt = mfma32(load_row_operand<D>(T, krow, s), qf[s], lt);
             float pf[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -260,11 +324,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             }
             const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
             // B operand: entries 32hs + c_row(0..7, gi) (+16), column 32c + n
-            const uint16_t *Tk = tile[t & 1] + 32 * hs * P;
 #pragma unroll
             for (int c = 0; c < DB; ++c) {
-                acc[c] = mfma32(a0, load_column_operand(Tk + 32 * c, ktr, P), acc[c]);
-                acc[c] = mfma32(a1, load_column_operand(Tk + 16 * P + 32 * c, ktr, P), acc[c]);
+                acc[c] = mfma32(a0, load_column_operand<D>(T, kcol, 0, c), acc[c]);
+                acc[c] = mfma32(a1, load_column_operand<D>(T, kcol, 16, c), acc[c]);
             }
         }
         }
@@ -282,12 +345,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const int hd = 32 * hb + n;
     if (gi == 0 && hd < a.H)
         a.dw[((int64_t)b * a.S + i) * a.H + hd] = a.scale * dw_sum;
+    // the weights of this lane's 16 heads, all loaded before the first store
+    // (a store in between would keep each load waiting on the previous one)
     const uint16_t *wrow = a.w + (int64_t)b * a.w_sb + (int64_t)i * a.w_ss;
+    uint16_t wh[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        wh[r] = wrow[min(32 * hb + c_row(r, gi), a.H - 1)];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int h = 32 * hb + c_row(r, gi);
         if (h < a.H) {
-            const float f = a.scale * bf16_to_f32(wrow[h]);
+            const float f = a.scale * bf16_to_f32(wh[r]);
             float *dst = a.dq + (((int64_t)b * a.H + h) * a.S + i) * D + n;
 #pragma unroll
             for (int c = 0; c < DB; ++c)
@@ -301,11 +370,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 
 template <int D, int HB>
 struct KeyGeom {
-    static constexpr int kPitch = D + 8;
     static constexpr int kHeads = 32 * HB;
     static constexpr int kChunks = kHeads * D / 8; // 16-byte pieces of one row's q block
     static constexpr int kPerThread = (kChunks + kBwdThreads - 1) / kBwdThreads;
-    static constexpr size_t kQBytes = (size_t)kHeads * kPitch * 2;
+    static constexpr size_t kQBytes = (size_t)kHeads * D * 2;
     static constexpr size_t kLdsBytes = 2 * kQBytes + 2 * (size_t)kHeads * 4;
 };
 
@@ -313,9 +381,10 @@ template <int D, int HB>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_keys_kernel(const BwdArgs a)
 {
     using G = KeyGeom<D, HB>;
-    constexpr int KS = D / 16, DB = D / 32, P = G::kPitch, NH = G::kHeads;
+    constexpr int KS = D / 16, DB = D / 32, NH = G::kHeads;
     extern __shared__ __attribute__((aligned(16))) unsigned char bwd_smem[];
-    // two buffers of one row's q block [NH][P] bf16, then two of its weights [NH] fp32
+    // two buffers of one row's q block [NH][D] bf16 (swizzled), then two of
+    // its weights [NH] fp32
     auto qbuf = [&](int buf) { return reinterpret_cast<uint16_t *>(bwd_smem + buf * G::kQBytes); };
     auto wbuf = [&](int buf) { return reinterpret_cast<float *>(bwd_smem + 2 * G::kQBytes + buf * NH * 4); };
 
@@ -357,9 +426,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     }
     const int kseg = a.k_seg ? a.k_seg[(int64_t)b * a.W + min(j, a.W - 1)] : 0;
 
-    // this lane's offset of the transposing reads of the q block: heads
-    // 16kb + c_row(0..7, gi), column n (plus 32hb heads and 32c columns)
-    const int qtr = tr_lane_offset(P);
+    // this lane's addressing of the q block: head n of a 32-head block
+    // (logits), heads c_row(0..7, gi) of a 16-head block, column n (dk)
+    const RowLane qrow = row_lane<D>(n, gi);
+    const ColLane qcol = col_lane<D>();
 
     f32x16 acc[DB];
 #pragma unroll
@@ -367,9 +437,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         for (int r = 0; r < 16; ++r)
             acc[c][r] = 0.0f;
 
+    // Staging of the next row: its q block and weights (as loaded, converted
+    // when stored) and this lane's gradient and segment id, which the row's
+    // iteration copies before the next loads are issued, so that no loaded
+    // value is used before the products that follow the loads.
     uint4 pre[G::kPerThread];
-    float wpre = 0.0f, gpre = 0.0f;
-    int spre = 0;
+    uint16_t wraw = 0;
+    float gnext = 0.0f;
+    int snext = 0;
     auto fetch = [&](int i) {
         const uint16_t *qrow = a.q + (int64_t)b * a.q_sb + (int64_t)i * a.q_ss;
 #pragma unroll
@@ -380,10 +455,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             if (c < G::kChunks && h < a.H)
                 pre[u] = *reinterpret_cast<const uint4 *>(qrow + (int64_t)h * a.q_sh + col);
         }
-        if (tid < NH)
-            wpre = tid < a.H ? bf16_to_f32(a.w[(int64_t)b * a.w_sb + (int64_t)i * a.w_ss + tid]) : 0.0f;
-        gpre = a.g[((int64_t)b * a.S + i) * a.W + min(j, a.W - 1)];
-        spre = a.q_seg ? a.q_seg[(int64_t)b * a.S + i] : 0;
+        if (tid < NH && tid < a.H)
+            wraw = a.w[(int64_t)b * a.w_sb + (int64_t)i * a.w_ss + tid];
+        gnext = a.g[((int64_t)b * a.S + i) * a.W + min(j, a.W - 1)];
+        if (a.q_seg)
+            snext = a.q_seg[(int64_t)b * a.S + i];
     };
     auto store = [&](int buf) {
 #pragma unroll
@@ -391,26 +467,23 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             const int c = tid + u * kBwdThreads;
             const int h = c / (D / 8), col = (c % (D / 8)) * 8;
             if (c < G::kChunks)
-                *reinterpret_cast<uint4 *>(qbuf(buf) + h * P + col) = pre[u];
+                *reinterpret_cast<uint4 *>(qbuf(buf) + tile_offset<D>(h, col / 8)) = pre[u];
         }
         if (tid < NH)
-            wbuf(buf)[tid] = wpre;
+            wbuf(buf)[tid] = bf16_to_f32(wraw); // heads past H: 0
     };
 
     fetch(i_lo);
     store(0);
-    float gcur = gpre;
-    int scur = spre;
+    // Every load issued so far completes here (see the row pass).
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int i = i_lo; i < c1; ++i) {
         const int buf = (i - i_lo) & 1;
-        const float g_i = gcur;
-        const int s_i = scur;
-        if (i + 1 < c1) {
+        const float g_i = gnext;
+        const int s_i = snext;
+        if (i + 1 < c1)
             fetch(i + 1);
-            gcur = gpre;
-            scur = spre;
-        }
         const int thr = visible_entries(off + i, a.m, a.W);
         bool ok = j < thr;
         if (a.k_seg)
@@ -423,6 +496,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             constexpr int kHbUnroll = HB == 4 ? 4 : 1;
 #pragma unroll kHbUnroll
             for (int hb = 0; hb < HB; ++hb) {
+                const uint16_t *Qh = Q + 32 * hb * D;
                 // logits: lane = entry n, register r = head 32hb + c_row(r, gi)
                 f32x16 lg;
 #pragma unroll
@@ -430,7 +504,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     lg[r] = 0.0f;
 #pragma unroll
                 for (int s = 0; s < KS; ++s)
-                    lg = mfma32(load_frag(Q + (32 * hb + n) * P + 16 * s + 8 * gi), kf[s], lg);
+                    lg = mfma32(load_row_operand<D>(Qh, qrow, s), kf[s], lg);
                 float pf[16];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
@@ -444,11 +518,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     }
                 }
                 const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
-                const uint16_t *Qh = Q + 32 * hb * P;
 #pragma unroll
                 for (int c = 0; c < DB; ++c) {
-                    acc[c] = mfma32(a0, load_column_operand(Qh + 32 * c, qtr, P), acc[c]);
-                    acc[c] = mfma32(a1, load_column_operand(Qh + 32 * c + 16 * P, qtr, P), acc[c]);
+                    acc[c] = mfma32(a0, load_column_operand<D>(Qh, qcol, 0, c), acc[c]);
+                    acc[c] = mfma32(a1, load_column_operand<D>(Qh, qcol, 16, c), acc[c]);
                 }
             }
         }
