@@ -277,6 +277,11 @@ csa_status check_backward(const csa_index_problem *p, Checked &c, csa_index_prob
     const int64_t red_blocks = ((int64_t)pa.B * pa.W * pa.D / 4 + 255) / 256;
     if (rows_blocks > 0x7FFFFFFF || key_blocks > 0x7FFFFFFF || red_blocks > 0x7FFFFFFF)
         return fail(CSA_ERR_UNSUPPORTED, "problem too large for one backward launch");
+    // the workspace size (partials + sign words) must fit in size_t
+    const unsigned __int128 part = (unsigned __int128)pa.B * chunks * pa.W * pa.D * 4;
+    const unsigned __int128 sign = (unsigned __int128)pa.B * pa.S * ((pa.W + 31) / 32) * pa.H * 4;
+    if (part + sign + 256 > (unsigned __int128)SIZE_MAX / 2)
+        return fail(CSA_ERR_UNSUPPORTED, "backward workspace too large");
     return CSA_OK;
 }
 
@@ -569,7 +574,7 @@ csa_status csa_index_backward_workspace_size(const csa_index_problem *p, size_t 
     csa_status st = check_backward(p, c, pa);
     if (st != CSA_OK)
         return st;
-    *bytes = csa::bwd_workspace_bytes(pa.B, pa.S, pa.W, pa.D);
+    *bytes = csa::bwd_workspace_bytes(pa.B, pa.S, pa.W, pa.D, pa.H);
     return ok();
 }
 
@@ -591,7 +596,7 @@ csa_status csa_index_score_backward(const csa_index_problem *p, const void *q, c
         return fail(CSA_ERR_INVALID_ARG, "dk must be a non-NULL, 16-byte aligned pointer");
     if (c.rows * pa.W > 0 && (!grad || !aligned(grad, 4)))
         return fail(CSA_ERR_INVALID_ARG, "grad must be a non-NULL, 4-byte aligned pointer");
-    const size_t need = csa::bwd_workspace_bytes(pa.B, pa.S, pa.W, pa.D);
+    const size_t need = csa::bwd_workspace_bytes(pa.B, pa.S, pa.W, pa.D, pa.H);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -613,6 +618,9 @@ csa_status csa_index_score_backward(const csa_index_problem *p, const void *q, c
     a.dk = dk;
     a.dw = dw;
     a.part = static_cast<float *>(workspace);
+    if (need > 0)
+        a.sign = reinterpret_cast<uint32_t *>(static_cast<unsigned char *>(workspace) +
+                                              csa::bwd_sign_offset(pa.B, pa.S, pa.W, pa.D));
     a.q_sb = pa.q_sb;
     a.q_sh = pa.q_sh;
     a.q_ss = pa.q_ss;
@@ -629,6 +637,7 @@ csa_status csa_index_score_backward(const csa_index_problem *p, const void *q, c
     a.scale = pa.scale;
     a.n_chunks = (pa.S + csa::kBwdChunkRows - 1) / csa::kBwdChunkRows;
     a.n_jtiles = (pa.W + csa::kBwdKeyTile - 1) / csa::kBwdKeyTile;
+    a.n_blk = (pa.W + 31) / 32;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = csa::launch_bwd_rows(pa.D, c.HB, a, s);
     if (e != hipSuccess)

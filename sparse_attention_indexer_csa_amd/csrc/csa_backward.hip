@@ -34,6 +34,10 @@ namespace csa {
 
 namespace {
 
+// The staging lambdas capture register arrays by reference: one left out of
+// line would move those arrays to scratch memory.
+#define CSA_INLINE __attribute__((always_inline))
+
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = kBwdWaves * kWave;
 
@@ -140,6 +144,14 @@ __device__ __forceinline__ bf16x8 load_column_operand(const uint16_t *tile, cons
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// bits = 2 * bits + (bit of this lane in mask): one v_addc_co_u32 with the
+// lane mask of a comparison as its carry-in (the compiler's own lowering of
+// that expression takes two or three instructions per bit).
+__device__ __forceinline__ void shift_in(uint32_t &bits, uint64_t mask)
+{
+    asm("v_addc_co_u32 %0, vcc, %0, %0, %1" : "+v"(bits) : "s"(mask) : "vcc");
+}
+
 __device__ __forceinline__ int64_t row_offset(const BwdArgs &a, int b)
 {
     return a.q_offset ? (int64_t)a.q_offset[b] : 0;
@@ -219,32 +231,50 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         for (int r = 0; r < 16; ++r)
             acc[c][r] = 0.0f;
     float dw_acc = 0.0f;
+    // logit-sign words of this row and this lane's head, as 16-bit halves
+    const bool n_head_ok = active && 32 * hb + n < a.H;
+    uint16_t *sign_row = reinterpret_cast<uint16_t *>(a.sign) +
+                         (((int64_t)b * a.S + (active ? i : 0)) * a.n_blk * a.H + 32 * hb + n) * 2;
 
     // this lane's addressing of the key tile: entry n of a 32-entry subtile
     // (logits), entries c_row(0..7, gi) of a 16-entry block, column n (dq)
     const RowLane krow = row_lane<D>(n, gi);
     const ColLane kcol = col_lane<D>();
     // Staging: piece c holds eight columns 8(c / kRowTile) .. +7 of entry
-    // c % kRowTile, so the lanes of a wave cover consecutive entries.
-    uint4 pre[G::kPerThread];
-    auto fetch = [&](int t) {
+    // c % kRowTile, so the lanes of a wave cover consecutive entries.  Entries
+    // past W repeat entry W - 1 (their gradient is zero; every entry of k
+    // below W must be finite).  The loads are unconditional, so that the waits
+    // for them are the same on every path: the tile after the last one
+    // repeats the last one and is never read.
+    u32x4 pre[G::kPerThread]; // a vector type: HIP's uint4 struct is copied through memory
+    int k_off[G::kPerThread]; // row * k_sw + col (< 2^30: k_sw < 2^24)
 #pragma unroll
-        for (int u = 0; u < G::kPerThread; ++u) {
-            const int c = tid + u * kBwdThreads;
-            const int row = c % kRowTile, col = (c / kRowTile) * 8;
-            const int j = kRowTile * t + row;
-            pre[u] = make_uint4(0, 0, 0, 0);
-            if (c < G::kChunks && j < a.W)
-                pre[u] = *reinterpret_cast<const uint4 *>(kb + (int64_t)j * a.k_sw + col);
+    for (int u = 0; u < G::kPerThread; ++u) {
+        const int c = min(tid + u * kBwdThreads, G::kChunks - 1);
+        k_off[u] = (c % kRowTile) * (int)a.k_sw + (c / kRowTile) * 8;
+    }
+    auto fetch = [&](int t) CSA_INLINE {
+        if (kRowTile * (t + 1) <= a.W) {
+            const uint16_t *kt = kb + (int64_t)kRowTile * t * a.k_sw;
+#pragma unroll
+            for (int u = 0; u < G::kPerThread; ++u)
+                pre[u] = *reinterpret_cast<const u32x4 *>(kt + k_off[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < G::kPerThread; ++u) {
+                const int c = min(tid + u * kBwdThreads, G::kChunks - 1);
+                const int j = min(kRowTile * t + c % kRowTile, a.W - 1);
+                pre[u] = *reinterpret_cast<const u32x4 *>(kb + (int64_t)j * a.k_sw + (c / kRowTile) * 8);
+            }
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](int buf) CSA_INLINE {
 #pragma unroll
         for (int u = 0; u < G::kPerThread; ++u) {
             const int c = tid + u * kBwdThreads;
             const int row = c % kRowTile, col = (c / kRowTile) * 8;
             if (c < G::kChunks)
-                *reinterpret_cast<uint4 *>(&tile[buf][tile_offset<D>(row, col / 8)]) = pre[u];
+                *reinterpret_cast<u32x4 *>(&tile[buf][tile_offset<D>(row, col / 8)]) = pre[u];
         }
     };
 
@@ -259,7 +289,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     float gnext = 0.0f; // gradient of this lane's next entry, as loaded
     int snext = 0;      // its segment id, as loaded
     bool gvis = false;  // whether the entry is before the row's threshold
-    auto fetch_g = [&](int t) {
+    auto fetch_g = [&](int t) CSA_INLINE {
         if (g_lane && active) {
             const int j = kRowTile * t + l;
             const int jc = min(j, a.W - 1);
@@ -269,11 +299,68 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             gnext = grow[jc];
         }
     };
-    auto store_g = [&](int buf) {
+    auto store_g = [&](int buf) CSA_INLINE {
         if (g_lane) {
             const bool ok = gvis && (!a.k_seg || snext == qseg);
             gtile[buf][wr][l] = ok ? gnext : 0.0f;
         }
+    };
+
+    // One key tile; P = t % 2 selects the LDS buffers, so that every LDS
+    // address is a lane offset plus a constant.
+    auto tile_step = [&](int t, auto P_) CSA_INLINE {
+        constexpr int P = decltype(P_)::value;
+        const int tn = min(t + 1, ntiles - 1);
+        fetch(tn);
+        fetch_g(tn);
+#pragma unroll
+        for (int hs = 0; hs < kRowTile / 32; ++hs) {
+            if (active && kRowTile * t + 32 * hs < thr) {
+                const uint16_t *T = tile[P] + 32 * hs * D;
+                // upstream gradient of this lane's 16 entries c_row(r, gi)
+                float ge[16];
+                const float *gt = gtile[P][wr] + 32 * hs;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 v = *reinterpret_cast<const float4 *>(gt + 8 * q4 + 4 * gi);
+                    ge[4 * q4 + 0] = v.x;
+                    ge[4 * q4 + 1] = v.y;
+                    ge[4 * q4 + 2] = v.z;
+                    ge[4 * q4 + 3] = v.w;
+                }
+                // transposed logits: lane = head n of this block, register r = entry c_row(r, gi)
+                f32x16 lt;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    lt[r] = 0.0f;
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    lt = mfma32(load_row_operand<D>(T, krow, s), qf[s], lt);
+                float pf[16];
+                uint32_t sbits = 0; // bit 15 - r: [l > 0] of entry c_row(r, gi)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float x = lt[r];
+                    dw_acc = fmaf(ge[r], relu(x), dw_acc);
+                    pf[r] = x > 0.0f ? ge[r] : 0.0f; // rounded to bf16 by operand_from
+                    shift_in(sbits, ballot(x > 0.0f));
+                }
+                // the signs go to the key pass: this lane's half (16 bits) of the
+                // word of head 32hb + n and the subtile's 32-entry block
+                if (n_head_ok)
+                    sign_row[(int64_t)(2 * t + hs) * a.H * 2 + gi] = (uint16_t)sbits;
+                const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
+                // B operand: entries 32hs + c_row(0..7, gi) (+16), column 32c + n
+#pragma unroll
+                for (int c = 0; c < DB; ++c) {
+                    acc[c] = mfma32(a0, load_column_operand<D>(T, kcol, 0, c), acc[c]);
+                    acc[c] = mfma32(a1, load_column_operand<D>(T, kcol, 16, c), acc[c]);
+                }
+            }
+        }
+        store(P ^ 1); // after the last tile: stored, never read
+        store_g(P ^ 1);
+        __syncthreads();
     };
 
     if (ntiles > 0) {
@@ -287,55 +374,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     // products never wait for them.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) {
-            fetch(t + 1);
-            fetch_g(t + 1);
-        }
-#pragma unroll
-        for (int hs = 0; hs < kRowTile / 32; ++hs) {
-        if (active && kRowTile * t + 32 * hs < thr) {
-            const uint16_t *T = tile[t & 1] + 32 * hs * D;
-            // upstream gradient of this lane's 16 entries c_row(r, gi)
-            float ge[16];
-            const float *gt = gtile[t & 1][wr] + 32 * hs;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 v = *reinterpret_cast<const float4 *>(gt + 8 * q4 + 4 * gi);
-                ge[4 * q4 + 0] = v.x;
-                ge[4 * q4 + 1] = v.y;
-                ge[4 * q4 + 2] = v.z;
-                ge[4 * q4 + 3] = v.w;
-            }
-            // transposed logits: lane = head n of this block, register r = entry c_row(r, gi)
-            f32x16 lt;
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                lt[r] = 0.0f;
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                lt = mfma32(load_row_operand<D>(T, krow, s), qf[s], lt);
-            float pf[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float x = lt[r];
-                dw_acc = fmaf(ge[r], relu(x), dw_acc);
-                pf[r] = x > 0.0f ? ge[r] : 0.0f; // rounded to bf16 by operand_from
-            }
-            const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
-            // B operand: entries 32hs + c_row(0..7, gi) (+16), column 32c + n
-#pragma unroll
-            for (int c = 0; c < DB; ++c) {
-                acc[c] = mfma32(a0, load_column_operand<D>(T, kcol, 0, c), acc[c]);
-                acc[c] = mfma32(a1, load_column_operand<D>(T, kcol, 16, c), acc[c]);
-            }
-        }
-        }
-        if (t + 1 < ntiles) {
-            store((t + 1) & 1);
-            store_g((t + 1) & 1);
-        }
-        __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+        tile_step(t, std::integral_constant<int, 0>());
+        if (t + 1 < ntiles)
+            tile_step(t + 1, std::integral_constant<int, 1>());
     }
 
     // lanes n and n + 32 hold the same head over different entries
@@ -373,20 +415,38 @@ struct KeyGeom {
     static constexpr int kHeads = 32 * HB;
     static constexpr int kChunks = kHeads * D / 8; // 16-byte pieces of one row's q block
     static constexpr int kPerThread = (kChunks + kBwdThreads - 1) / kBwdThreads;
+    static constexpr int kBlocks = kBwdKeyTile / 32;  // 32-entry blocks of a key tile (one per wave)
+    static constexpr int kSignWords = kBlocks * kHeads; // sign words of one row and one key tile
+    static constexpr int kSignPerThread = (kSignWords + kBwdThreads - 1) / kBwdThreads;
     static constexpr size_t kQBytes = (size_t)kHeads * D * 2;
-    static constexpr size_t kLdsBytes = 2 * kQBytes + 2 * (size_t)kHeads * 4;
+    static constexpr size_t kWBytes = (size_t)kHeads * 4;
+    static constexpr size_t kSBytes = (size_t)kSignWords * 4;
+    static constexpr size_t kLdsBytes = 2 * (kQBytes + kWBytes + kSBytes);
 };
+
+// Position, in a sign word, of the bit of entry e (0..31) of its block: the
+// row pass writes the 16 bits of entries c_row(0..15, g) of lane half g as
+// bits 16g + 15 - r.
+__device__ __forceinline__ int sign_bit_of_entry(int e)
+{
+    const int g = (e >> 2) & 1, r = 4 * (e >> 3) + (e & 3); // e = c_row(r, g)
+    return 16 * g + 15 - r;
+}
 
 template <int D, int HB>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_keys_kernel(const BwdArgs a)
 {
     using G = KeyGeom<D, HB>;
-    constexpr int KS = D / 16, DB = D / 32, NH = G::kHeads;
+    constexpr int DB = D / 32, NH = G::kHeads;
+    static_assert(G::kBlocks == kBwdWaves, "one 32-entry block per wave");
     extern __shared__ __attribute__((aligned(16))) unsigned char bwd_smem[];
-    // two buffers of one row's q block [NH][D] bf16 (swizzled), then two of
-    // its weights [NH] fp32
+    // two buffers each of one row's q block [NH][D] bf16 (swizzled), its
+    // weights [NH] fp32 and its sign words [kBlocks][NH]
     auto qbuf = [&](int buf) { return reinterpret_cast<uint16_t *>(bwd_smem + buf * G::kQBytes); };
-    auto wbuf = [&](int buf) { return reinterpret_cast<float *>(bwd_smem + 2 * G::kQBytes + buf * NH * 4); };
+    auto wbuf = [&](int buf) { return reinterpret_cast<float *>(bwd_smem + 2 * G::kQBytes + buf * G::kWBytes); };
+    auto sbuf = [&](int buf) {
+        return reinterpret_cast<uint32_t *>(bwd_smem + 2 * (G::kQBytes + G::kWBytes) + buf * G::kSBytes);
+    };
 
     // Workgroup -> (batch, chunk, key tile).  Workgroups are dealt to the 8
     // XCDs in turn; XCD x takes every 8th chunk (latest rows first) with all
@@ -413,22 +473,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const int wv = uniform(tid / kWave);
     const int l = lane(), n = l & 31, gi = l >> 5;
     const int jw = j0 + 32 * wv; // this wave's first entry
-    const int j = jw + n;        // this lane's entry (logit column, dk A row)
+    const int j = jw + n;        // this lane's entry (dk A row)
     const bool wave_has = jw < a.W;
-
-    // B operand of the logits: this lane's entry, eight values of D per k-step.
-    bf16x8 kf[KS];
-    {
-        const uint16_t *kp = a.k + (int64_t)b * a.k_sb + (int64_t)min(j, a.W - 1) * a.k_sw + 8 * gi;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            kf[s] = j < a.W ? load_frag(kp + 16 * s) : zero_frag();
-    }
     const int kseg = a.k_seg ? a.k_seg[(int64_t)b * a.W + min(j, a.W - 1)] : 0;
+    const int sbit = sign_bit_of_entry(n);
 
-    // this lane's addressing of the q block: head n of a 32-head block
-    // (logits), heads c_row(0..7, gi) of a 16-head block, column n (dk)
-    const RowLane qrow = row_lane<D>(n, gi);
+    // this lane's addressing of the q block: heads c_row(0..7, gi) of a
+    // 16-head block, column n
     const ColLane qcol = col_lane<D>();
 
     f32x16 acc[DB];
@@ -437,84 +488,151 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         for (int r = 0; r < 16; ++r)
             acc[c][r] = 0.0f;
 
-    // Staging of the next row: its q block and weights (as loaded, converted
-    // when stored) and this lane's gradient and segment id, which the row's
-    // iteration copies before the next loads are issued, so that no loaded
-    // value is used before the products that follow the loads.
-    uint4 pre[G::kPerThread];
+    // Staging.  The q block and the weights of row i + 1 (shared by every key
+    // tile of the chunk, so mostly L2 hits) are loaded during row i; the sign
+    // words, this lane's gradient and the row's segment id (read once, from
+    // HBM) two rows ahead, in two register slots that alternate with the
+    // parity of the row.  No loaded value is used before the products that
+    // follow its load: the loads are unconditional (clamped addresses) and
+    // what lies outside the problem is zeroed when stored, the weights are
+    // converted when stored, and slot P is read at the top of its row before
+    // the next load into it is issued.  The far loads are issued after the q
+    // block's, so that waiting for the q block leaves them in flight.
+    // The row addresses advance by one row's stride per step (wave-uniform
+    // pointer bumps, no 64-bit index products in the loop), and so does the
+    // causal threshold (no division in the loop).
+    u32x4 pre[G::kPerThread]; // a vector type: HIP's uint4 struct is copied through memory
     uint16_t wraw = 0;
-    float gnext = 0.0f;
-    int snext = 0;
-    auto fetch = [&](int i) {
-        const uint16_t *qrow = a.q + (int64_t)b * a.q_sb + (int64_t)i * a.q_ss;
+    uint32_t sgn[2][G::kSignPerThread];
+    float gsl[2] = {0.0f, 0.0f};
+    int ssl[2] = {0, 0};
+    const int blk0 = j0 / 32;
+    // per-thread offsets within a row (loop invariant)
+    int64_t q_off[G::kPerThread];
 #pragma unroll
-        for (int u = 0; u < G::kPerThread; ++u) {
-            const int c = tid + u * kBwdThreads;
-            const int h = c / (D / 8), col = (c % (D / 8)) * 8;
-            pre[u] = make_uint4(0, 0, 0, 0);
-            if (c < G::kChunks && h < a.H)
-                pre[u] = *reinterpret_cast<const uint4 *>(qrow + (int64_t)h * a.q_sh + col);
+    for (int u = 0; u < G::kPerThread; ++u) {
+        const int c = min(tid + u * kBwdThreads, G::kChunks - 1);
+        q_off[u] = (int64_t)min(c / (D / 8), a.H - 1) * a.q_sh + (c % (D / 8)) * 8;
+    }
+    int s_off[G::kSignPerThread];
+#pragma unroll
+    for (int u = 0; u < G::kSignPerThread; ++u) {
+        const int c = tid + u * kBwdThreads;
+        s_off[u] = min(blk0 + c / NH, a.n_blk - 1) * a.H + min(c % NH, a.H - 1);
+    }
+    const int g_off = min(j, a.W - 1);
+    const bool w_lane = tid < NH && tid < a.H;
+    // near rows (q block, weights) and far rows (signs, gradient, segment id)
+    const int64_t bs = (int64_t)b * a.S;
+    const uint16_t *q_row = a.q + (int64_t)b * a.q_sb + (int64_t)i_lo * a.q_ss;
+    const uint16_t *w_row = a.w + (int64_t)b * a.w_sb + (int64_t)i_lo * a.w_ss;
+    const uint32_t *s_row = a.sign + (bs + i_lo) * a.n_blk * a.H;
+    const float *g_row = a.g + (bs + i_lo) * a.W;
+    // without segments the first word of g is read instead and never used
+    // (the load is unconditional like the others)
+    const int32_t *seg_row = a.q_seg ? a.q_seg + bs + i_lo : reinterpret_cast<const int32_t *>(a.g);
+    const int64_t s_stride = (int64_t)a.n_blk * a.H;
+    const int seg_stride = a.q_seg ? 1 : 0;
+    int near_row = i_lo, far_row = i_lo;
+    // next row of each kind, clamped to the chunk's last row
+    auto next_near = [&]() CSA_INLINE {
+        if (near_row + 1 < c1) {
+            ++near_row;
+            q_row += a.q_ss;
+            w_row += a.w_ss;
         }
-        if (tid < NH && tid < a.H)
-            wraw = a.w[(int64_t)b * a.w_sb + (int64_t)i * a.w_ss + tid];
-        gnext = a.g[((int64_t)b * a.S + i) * a.W + min(j, a.W - 1)];
-        if (a.q_seg)
-            snext = a.q_seg[(int64_t)b * a.S + i];
     };
-    auto store = [&](int buf) {
+    auto next_far = [&]() CSA_INLINE {
+        if (far_row + 1 < c1) {
+            ++far_row;
+            s_row += s_stride;
+            g_row += a.W;
+            seg_row += seg_stride;
+        }
+    };
+    auto fetch_q = [&]() CSA_INLINE {
+#pragma unroll
+        for (int u = 0; u < G::kPerThread; ++u)
+            pre[u] = *reinterpret_cast<const u32x4 *>(q_row + q_off[u]);
+        if (w_lane)
+            wraw = w_row[tid];
+    };
+    auto fetch_far = [&](uint32_t (&sp)[G::kSignPerThread], float &gv, int &sv) {
+#pragma unroll
+        for (int u = 0; u < G::kSignPerThread; ++u)
+            sp[u] = s_row[s_off[u]];
+        gv = g_row[g_off];
+        sv = *seg_row;
+    };
+    auto store = [&](int buf, const uint32_t (&sp)[G::kSignPerThread]) {
 #pragma unroll
         for (int u = 0; u < G::kPerThread; ++u) {
             const int c = tid + u * kBwdThreads;
             const int h = c / (D / 8), col = (c % (D / 8)) * 8;
             if (c < G::kChunks)
-                *reinterpret_cast<uint4 *>(qbuf(buf) + tile_offset<D>(h, col / 8)) = pre[u];
+                *reinterpret_cast<u32x4 *>(qbuf(buf) + tile_offset<D>(h, col / 8)) =
+                    h < a.H ? pre[u] : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < G::kSignPerThread; ++u) {
+            const int c = tid + u * kBwdThreads;
+            if (c < G::kSignWords)
+                sbuf(buf)[c] = (c % NH < a.H && blk0 + c / NH < a.n_blk) ? sp[u] : 0u;
         }
         if (tid < NH)
             wbuf(buf)[tid] = bf16_to_f32(wraw); // heads past H: 0
     };
+    // causal threshold of row i: clamp(floor((off + i + 1) / m), 0, W),
+    // carried as quotient and remainder
+    int64_t thr_q = floor_div_pos(off + i_lo + 1, a.m);
+    int thr_r = (int)(off + i_lo + 1 - thr_q * a.m);
 
-    fetch(i_lo);
-    store(0);
-    // Every load issued so far completes here (see the row pass).
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int i = i_lo; i < c1; ++i) {
-        const int buf = (i - i_lo) & 1;
-        const float g_i = gnext;
-        const int s_i = snext;
-        if (i + 1 < c1)
-            fetch(i + 1);
-        const int thr = visible_entries(off + i, a.m, a.W);
+    // One row: P = (i - i_lo) % 2 selects the LDS buffers and the slot.
+    // Loads: near row i + 1, far row i + 2 (clamped; rows past the chunk are
+    // loaded and never used, so that the waits are the same on every path).
+    auto row_step = [&](int i, auto P_) CSA_INLINE {
+        constexpr int P = decltype(P_)::value;
+        const float g_i = gsl[P];
+        const int s_i = ssl[P];
+        next_near();
+        fetch_q();
+        next_far();
+        fetch_far(sgn[P], gsl[P], ssl[P]);
+        const int thr = (int)min(max(thr_q, (int64_t)0), (int64_t)a.W);
+        if (++thr_r == a.m) {
+            thr_r = 0;
+            ++thr_q;
+        }
         bool ok = j < thr;
         if (a.k_seg)
             ok = ok && kseg == s_i;
         const float ge = ok ? g_i : 0.0f;
         if (wave_has && ballot(ok) != 0) {
-            const uint16_t *Q = qbuf(buf);
-            const float *Wt = wbuf(buf);
+            const uint16_t *Q = qbuf(P);
+            const float *Wt = wbuf(P);
+            const uint32_t *Sg = sbuf(P) + wv * NH;
             // rolled for two head blocks (fewer live registers), unrolled for four
             constexpr int kHbUnroll = HB == 4 ? 4 : 1;
 #pragma unroll kHbUnroll
             for (int hb = 0; hb < HB; ++hb) {
                 const uint16_t *Qh = Q + 32 * hb * D;
-                // logits: lane = entry n, register r = head 32hb + c_row(r, gi)
-                f32x16 lg;
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    lg[r] = 0.0f;
-#pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    lg = mfma32(load_row_operand<D>(Qh, qrow, s), kf[s], lg);
+                // A operand of the dk product, lane = entry n, k index r =
+                // head 32hb + c_row(r, gi): g w [l > 0], with the sign of l
+                // as the row pass found it
                 float pf[16];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     // c_row(4 q4 + c, gi) = 8 q4 + 4 gi + c: four consecutive heads
                     const float4 wq = *reinterpret_cast<const float4 *>(Wt + 32 * hb + 8 * q4 + 4 * gi);
+                    const uint4 sq = *reinterpret_cast<const uint4 *>(Sg + 32 * hb + 8 * q4 + 4 * gi);
                     const float wr[4] = {wq.x, wq.y, wq.z, wq.w};
+                    const uint32_t sw[4] = {sq.x, sq.y, sq.z, sq.w};
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        const int r = 4 * q4 + c;
-                        pf[r] = lg[r] > 0.0f ? ge * wr[c] : 0.0f; // rounded to bf16 by operand_from
+                        // all ones when the logit is positive, else zero
+                        const int32_t pos = __builtin_amdgcn_sbfe((int32_t)sw[c], sbit, 1);
+                        // rounded to bf16 by operand_from
+                        pf[4 * q4 + c] = __int_as_float(pos & __float_as_int(ge * wr[c]));
                     }
                 }
                 const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
@@ -525,9 +643,22 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 }
             }
         }
-        if (i + 1 < c1)
-            store(buf ^ 1);
+        store(P ^ 1, sgn[P ^ 1]); // after the last row: stored, never read
         __syncthreads();
+    };
+
+    fetch_q();
+    fetch_far(sgn[0], gsl[0], ssl[0]);
+    next_far();
+    fetch_far(sgn[1], gsl[1], ssl[1]);
+    store(0, sgn[0]);
+    // Every load issued so far completes here (see the row pass).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int i = i_lo; i < c1; i += 2) {
+        row_step(i, std::integral_constant<int, 0>());
+        if (i + 1 < c1)
+            row_step(i + 1, std::integral_constant<int, 1>());
     }
 
     // partial[b, chunk, entry, d]: lane = column 32c + n, register r = entry jw + c_row(r, gi)

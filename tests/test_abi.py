@@ -206,14 +206,16 @@ def test_backward_workspace_and_validation(lib):
     n = ctypes.c_size_t(0)
     p = prob(B=2, S=600, H=4, D=32, W=40)
     assert lib.csa_index_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == OK
-    assert n.value == 2 * 3 * 40 * 32 * 4  # B * ceil(S/256) row chunks * W * D fp32 partials
+    # B * ceil(S/256) row chunks * W * D fp32 partials (30720 bytes, a multiple
+    # of 256), then B * S * ceil(W/32) * H 32-bit logit-sign words
+    assert n.value == 2 * 3 * 40 * 32 * 4 + 2 * 600 * 2 * 4 * 4
     assert lib.csa_index_backward_workspace_size(ctypes.byref(prob(D=40)), ctypes.byref(n)) == UNSUPPORTED
     assert lib.csa_index_backward_workspace_size(None, ctypes.byref(n)) == INVALID
     # the plan field is not used by the backward
     assert lib.csa_index_backward_workspace_size(ctypes.byref(prob(W=70000, plan=1)), ctypes.byref(n)) == OK
 
     p = prob()
-    need = 16 * 8 * 4 * 1  # one chunk of W=8 entries x D=32
+    need = 8 * 32 * 4 + 16 * 4 * 4  # one chunk of W=8 entries x D=32, then 16 rows x 4 heads of sign words
     m = masks()
 
     def call(q=FAKE, k=FAKE, w=FAKE, g=FAKE, dq=FAKE, dk=FAKE, dw=FAKE, ws=FAKE, wsb=need * 2, pp=p):
