@@ -341,8 +341,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float x = lt[r];
-                    dw_acc = fmaf(ge[r], relu(x), dw_acc);
                     pf[r] = x > 0.0f ? ge[r] : 0.0f; // rounded to bf16 by operand_from
+                    // g ReLU(x) accumulated as (g [x > 0]) x: the same value
+                    // for finite x (x <= 0 adds a zero), one instruction fewer
+                    dw_acc = fmaf(pf[r], x, dw_acc);
                     shift_in(sbits, ballot(x > 0.0f));
                 }
                 // the signs go to the key pass: this lane's half (16 bits) of the
