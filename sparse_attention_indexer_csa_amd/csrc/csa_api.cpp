@@ -242,7 +242,7 @@ csa_status launch_topk_rows(csa::KernelArgs &a, hipStream_t s)
     if (st != CSA_OK)
         return st;
     const int lim = d.lds;
-    size_t block_lds = csa::topk_block_lds_bytes(a.cap, a.top_k);
+    size_t block_lds = csa::topk_block_lds_bytes(a.cap, a.top_k, a.W);
     if (a.W >= csa::kTopkBlockMinLen && block_lds <= (size_t)lim)
         return launched(csa::launch_topk_block(a, block_lds, s), "top-k");
     size_t lds = csa::topk_lds_bytes(a.cap);

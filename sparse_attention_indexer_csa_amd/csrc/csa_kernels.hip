@@ -1056,6 +1056,239 @@ __device__ __forceinline__ uint32_t coarse_threshold(const float *src, int n, in
     return coarse_find<NW>(hist, k, part);
 }
 
+// Fast path of the long-row top-k for rows of at most kTopkBlockWaves * 64 *
+// EPT entries: the row is read once into registers (EPT keys per thread, entry
+// e * threads + t in thread t), the coarse histogram gives the bucket of the
+// k-th largest key, the keys above that bucket's lower bound (the candidates,
+// usually a few hundred) are compacted into LDS, and all waves sort them at
+// once with a bitonic network on 64-bit composites (key, ~entry), so that
+// equal keys come out in entry order.  The first k sorted positions are the
+// selection.  Returns false, having written nothing, when there are more
+// than kBlockCandMax candidates.
+constexpr int kBlockCandMax = 2048;
+
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int lx)
+{
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    switch (lx) {
+    case 1: lo = lane_xor_u32<1>(lo); hi = lane_xor_u32<1>(hi); break;
+    case 2: lo = lane_xor_u32<2>(lo); hi = lane_xor_u32<2>(hi); break;
+    case 4: lo = lane_xor_u32<4>(lo); hi = lane_xor_u32<4>(hi); break;
+    case 8: lo = lane_xor_u32<8>(lo); hi = lane_xor_u32<8>(hi); break;
+    case 16: lo = lane_xor_u32<16>(lo); hi = lane_xor_u32<16>(hi); break;
+    default: lo = lane_xor_u32<32>(lo); hi = lane_xor_u32<32>(hi); break;
+    }
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// One compare-exchange step between registers r and r + S of each thread
+// (S < PER) in a merge of blocks of `size`.
+template <int PER, int S>
+__device__ __forceinline__ void cex_regs(uint64_t (&v)[PER], int t, int size)
+{
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        if ((r & S) == 0) {
+            const bool desc = ((t * PER + r) & size) == 0;
+            const uint64_t x = v[r], y = v[r + S];
+            v[r] = desc ? max(x, y) : min(x, y);
+            v[r + S] = desc ? min(x, y) : max(x, y);
+        }
+    }
+}
+
+// Descending bitonic sort of N = PER * threads composites, PER per thread at
+// positions t * PER + r.  Partners within a thread are exchanged in
+// registers, within a wave by lane exchanges, across waves through sb
+// (N 64-bit words of LDS).  Fully unrolled: every stride and direction is a
+// constant or a bit of the thread index.
+template <int PER>
+__device__ __forceinline__ void block_bitonic_desc(uint64_t (&v)[PER], uint64_t *sb)
+{
+    constexpr int NT = kTopkBlockWaves * kWave, N = PER * NT;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int size = 2; size <= N; size *= 2) {
+#pragma unroll
+        for (int stride = size / 2; stride > 0; stride /= 2) {
+            if (stride < PER) {
+                if constexpr (PER >= 2) {
+                    if (stride == 1)
+                        cex_regs<PER, 1>(v, t, size);
+                }
+                if constexpr (PER >= 4) {
+                    if (stride == 2)
+                        cex_regs<PER, 2>(v, t, size);
+                }
+            } else if (stride < PER * kWave) {
+#pragma unroll
+                for (int r = 0; r < PER; ++r) {
+                    const int p = t * PER + r;
+                    const bool keep_max = ((p & stride) == 0) == ((p & size) == 0);
+                    const uint64_t y = lane_xor_u64(v[r], stride / PER);
+                    v[r] = keep_max ? max(v[r], y) : min(v[r], y);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < PER; ++r)
+                    sb[t * PER + r] = v[r];
+                __syncthreads();
+                uint64_t y[PER];
+#pragma unroll
+                for (int r = 0; r < PER; ++r)
+                    y[r] = sb[(t * PER + r) ^ stride];
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < PER; ++r) {
+                    const int p = t * PER + r;
+                    const bool keep_max = ((p & stride) == 0) == ((p & size) == 0);
+                    v[r] = keep_max ? max(v[r], y[r]) : min(v[r], y[r]);
+                }
+            }
+        }
+    }
+}
+
+template <int PER>
+__device__ __forceinline__ void block_sort_write(const uint32_t *ckey, const uint32_t *cent, int m, int k,
+                                                 uint64_t *sb, int32_t *out)
+{
+    const int t = threadIdx.x;
+    uint64_t v[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const int p = t * PER + r;
+        v[r] = p < m ? ((uint64_t)ckey[p] << 32) | (uint32_t)(0xFFFFFFFFu - cent[p]) : 0ull;
+    }
+    __syncthreads(); // sb overlaps the candidate arrays
+    block_bitonic_desc<PER>(v, sb);
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const int p = t * PER + r;
+        if (p < k)
+            out[p] = p < m ? (int32_t)(0xFFFFFFFFu - (uint32_t)v[r]) : -1;
+    }
+    for (int p = PER * kTopkBlockWaves * kWave + t; p < k; p += kTopkBlockWaves * kWave)
+        out[p] = -1;
+}
+
+// Rows up to this length take the fast path: the row's keys fit in LDS.
+constexpr int kTopkBlockFastMaxW = 32768;
+
+// LDS of the fast path: the coarse histogram (later the candidates),
+// the row's keys (later the sort buffer), the counters.
+__host__ __device__ constexpr size_t topk_block_fast_lds_bytes(int W)
+{
+    return (size_t)kCoarseBins * 4 + (size_t)(W + 3) / 4 * 16 + 64;
+}
+
+__device__ __forceinline__ bool topk_block_fast(const float *src, int n, int k, unsigned char *smem, int32_t *out)
+{
+    constexpr int NW = kTopkBlockWaves, NT = NW * kWave, kB = 4;
+    static_assert(2 * kBlockCandMax * 4 <= kCoarseBins * 4, "candidates fit the histogram's place");
+    uint32_t *hist = reinterpret_cast<uint32_t *>(smem);
+    uint32_t *ckey = hist, *cent = hist + kBlockCandMax;
+    uint32_t *row = hist + kCoarseBins;
+    const int n4 = (n + 3) / 4;
+    int *part = reinterpret_cast<int *>(row + 4 * n4);
+    int *count = part + NW + 1;
+    const int t = threadIdx.x, l = lane();
+
+    // pass 1: the keys to LDS and the coarse histogram
+    coarse_clear<NW>(hist);
+    __syncthreads();
+    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
+    const int nv = vec ? n / 4 : 0;
+    const float4 *src4 = reinterpret_cast<const float4 *>(src);
+    u32x4 *row4 = reinterpret_cast<u32x4 *>(row);
+#pragma unroll 1
+    for (int i0 = 0; i0 < nv; i0 += 8 * NT) {
+        float4 v[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const int i = i0 + x * NT + t;
+            v[x] = i < nv ? src4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const int i = i0 + x * NT + t;
+            const u32x4 kv = {score_key(v[x].x), score_key(v[x].y), score_key(v[x].z), score_key(v[x].w)};
+            if (i < nv)
+                row4[i] = kv;
+            coarse_add(hist, kv.x);
+            coarse_add(hist, kv.y);
+            coarse_add(hist, kv.z);
+            coarse_add(hist, kv.w);
+        }
+    }
+    for (int j = nv * 4 + t; j < n; j += NT) {
+        const uint32_t kv = score_key(src[j]);
+        row[j] = kv;
+        coarse_add(hist, kv);
+    }
+    __syncthreads();
+    // candidates: the keys in (tau, kKeyPosInf]
+    const uint32_t tau = coarse_find<NW>(hist, k, part);
+    const uint32_t lo = tau + 1u, span = kKeyPosInf - lo;
+    if (t == 0)
+        *count = 0;
+    __syncthreads();
+    // pass 2 over the LDS row: append the candidates (in any order: the sort
+    // orders them), one atomic per wave and batch
+#pragma unroll 1
+    for (int i0 = 0; i0 < n4; i0 += kB * NT) {
+        u32x4 kv[kB];
+        int c = 0;
+#pragma unroll
+        for (int x = 0; x < kB; ++x) {
+            const int i = i0 + x * NT + t;
+            kv[x] = i < n4 ? row4[i] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (4 * i + e >= n)
+                    kv[x][e] = 0u; // past the row: never a candidate
+                c += (kv[x][e] - lo <= span) ? 1 : 0;
+            }
+        }
+        const int incl = wave_inclusive_sum(c);
+        const int wave_total = read_lane(incl, kWave - 1);
+        if (wave_total > 0) {
+            int base = 0;
+            if (l == kWave - 1)
+                base = atomicAdd(count, wave_total);
+            int slot = read_lane(base, kWave - 1) + incl - c;
+#pragma unroll
+            for (int x = 0; x < kB; ++x) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (kv[x][e] - lo <= span) {
+                        if (slot < kBlockCandMax) {
+                            ckey[slot] = kv[x][e];
+                            cent[slot] = (uint32_t)(4 * (i0 + x * NT + t) + e);
+                        }
+                        ++slot;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int m = *count;
+    if (m > kBlockCandMax)
+        return false;
+    // the sort buffer takes the row's place: the LDS holds W >= 8192 keys on
+    // this path, at least the 16 KB of 2048 composites (it may cover the
+    // counters, which are not read again)
+    uint64_t *sb = reinterpret_cast<uint64_t *>(row);
+    if (m <= NT)
+        block_sort_write<1>(ckey, cent, m, k, sb, out);
+    else if (m <= 2 * NT)
+        block_sort_write<2>(ckey, cent, m, k, sb, out);
+    else
+        block_sort_write<4>(ckey, cent, m, k, sb, out);
+    return true;
+}
+
 __global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(const KernelArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -1075,6 +1308,13 @@ __global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(con
     const int per = (chunks + kTopkBlockWaves - 1) / kTopkBlockWaves;
     const int j0 = min(wv * per * kWave, n), j1 = min((wv + 1) * per * kWave, n);
     const float *src = a.scores + row * a.W;
+    // Rows whose keys fit in LDS (the workgroup has the LDS for W keys) take
+    // the fast path unless it finds too many candidates.
+    if (a.W <= kTopkBlockFastMaxW) {
+        if (topk_block_fast(src, n, a.top_k, smem, a.idx + row * a.top_k))
+            return;
+        __syncthreads(); // the streaming path below reuses the same LDS
+    }
     TopKRow<uint32_t> tk;
     {
         const uint32_t tau0 = coarse_threshold<kTopkBlockWaves>(src, n, a.top_k, hist_all, cnt);
@@ -1192,9 +1432,11 @@ size_t rows_lds_bytes(int D, int HB, int mode, int cap)
 
 size_t topk_lds_bytes(int cap) { return (size_t)kTopkWaves * (1024 + (size_t)cap * 8); }
 
-size_t topk_block_lds_bytes(int cap, int top_k)
+size_t topk_block_lds_bytes(int cap, int top_k, int W)
 {
-    return (size_t)kTopkBlockWaves * (1024 + (size_t)cap * 8) + (kTopkBlockWaves + 2) * 4 + (size_t)top_k * 8;
+    const size_t stream = (size_t)kTopkBlockWaves * (1024 + (size_t)cap * 8) + (kTopkBlockWaves + 2) * 4 +
+                          (size_t)top_k * 8;
+    return W <= kTopkBlockFastMaxW ? max(stream, topk_block_fast_lds_bytes(W)) : stream;
 }
 
 template <typename K>

@@ -71,7 +71,7 @@ constexpr int kRowTilesMaxW = 65536;
 
 size_t rows_lds_bytes(int D, int HB, int mode, int cap);
 size_t topk_lds_bytes(int cap);
-size_t topk_block_lds_bytes(int cap, int top_k);
+size_t topk_block_lds_bytes(int cap, int top_k, int W);
 
 // Each returns hipSuccess or the launch error; nothing is synchronised.
 hipError_t launch_rows(int D, int HB, int mode, const KernelArgs &a, size_t lds, hipStream_t s);
