@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 #include <string>
 
@@ -91,7 +92,8 @@ csa_status check_problem(const csa_index_problem *p, Checked &c)
                     (long long)p->k_sw, (long long)kMaxKeyStride);
     c.rows = (int64_t)p->B * p->S;
     c.HB = head_blocks(p->H);
-    int64_t row_blocks = (int64_t)p->B * ((p->S + csa::kRowsPerBlock - 1) / csa::kRowsPerBlock);
+    // sizes up to INT32_MAX: ceiling divisions in 64 bits
+    int64_t row_blocks = (int64_t)p->B * (((int64_t)p->S + csa::kRowsPerBlock - 1) / csa::kRowsPerBlock);
     int plan = p->plan;
     if (plan == CSA_PLAN_AUTO)
         plan = ((row_blocks < kMinRowBlocks && p->W >= kMinSplitW) || p->W > csa::kRowTilesMaxW)
@@ -101,7 +103,7 @@ csa_status check_problem(const csa_index_problem *p, Checked &c)
         return fail(CSA_ERR_UNSUPPORTED, "the row-tile plan takes W <= %d (got %d)", csa::kRowTilesMaxW, p->W);
     c.plan = plan;
     // grid sizes must fit a 32-bit launch
-    int64_t chunks = (p->W + csa::kSplitChunk - 1) / csa::kSplitChunk;
+    int64_t chunks = ((int64_t)p->W + csa::kSplitChunk - 1) / csa::kSplitChunk;
     if (row_blocks > 0x7FFFFFFF || c.rows * (chunks > 0 ? chunks : 1) > 0x7FFFFFFF)
         return fail(CSA_ERR_UNSUPPORTED, "problem too large for one launch");
     return CSA_OK;
@@ -159,8 +161,8 @@ csa::KernelArgs make_args(const csa_index_problem *p, const Checked &c, const vo
     a.W = p->W;
     a.m = p->compress_rate;
     a.scale = p->scale;
-    a.n_row_blocks = (p->S + csa::kRowsPerBlock - 1) / csa::kRowsPerBlock;
-    a.n_chunks = (p->W + csa::kSplitChunk - 1) / csa::kSplitChunk;
+    a.n_row_blocks = (int)(((int64_t)p->S + csa::kRowsPerBlock - 1) / csa::kRowsPerBlock);
+    a.n_chunks = (int)(((int64_t)p->W + csa::kSplitChunk - 1) / csa::kSplitChunk);
     return a;
 }
 
@@ -272,14 +274,14 @@ csa_status check_backward(const csa_index_problem *p, Checked &c, csa_index_prob
     const int rpw = 4 / c.HB;
     const int64_t chunks = ((int64_t)pa.S + csa::kBwdChunkRows - 1) / csa::kBwdChunkRows;
     const int64_t jtiles = ((int64_t)pa.W + csa::kBwdKeyTile - 1) / csa::kBwdKeyTile;
-    const int64_t rows_blocks = (int64_t)pa.B * ((pa.S + rpw - 1) / rpw);
+    const int64_t rows_blocks = (int64_t)pa.B * (((int64_t)pa.S + rpw - 1) / rpw);
     const int64_t key_blocks = (int64_t)pa.B * 8 * ((chunks + 7) / 8) * jtiles;
     const int64_t red_blocks = ((int64_t)pa.B * pa.W * pa.D / 4 + 255) / 256;
     if (rows_blocks > 0x7FFFFFFF || key_blocks > 0x7FFFFFFF || red_blocks > 0x7FFFFFFF)
         return fail(CSA_ERR_UNSUPPORTED, "problem too large for one backward launch");
     // the workspace size (partials + sign words) must fit in size_t
     const unsigned __int128 part = (unsigned __int128)pa.B * chunks * pa.W * pa.D * 4;
-    const unsigned __int128 sign = (unsigned __int128)pa.B * pa.S * ((pa.W + 31) / 32) * pa.H * 4;
+    const unsigned __int128 sign = (unsigned __int128)pa.B * pa.S * (((int64_t)pa.W + 31) / 32) * pa.H * 4;
     if (part + sign + 256 > (unsigned __int128)SIZE_MAX / 2)
         return fail(CSA_ERR_UNSUPPORTED, "backward workspace too large");
     return CSA_OK;
@@ -330,7 +332,11 @@ int32_t csa_index_abi_version(void) { return CSA_INDEX_ABI_VERSION; }
 
 const char *csa_status_string(csa_status s)
 {
-    switch (s) {
+    // read as an int: a C caller may pass any value, and loading an enum
+    // outside its enumerators' range is undefined in C++
+    int v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
     case CSA_OK: return "ok";
     case CSA_ERR_INVALID_ARG: return "invalid argument";
     case CSA_ERR_UNSUPPORTED: return "unsupported shape or layout";
@@ -635,9 +641,9 @@ csa_status csa_index_score_backward(const csa_index_problem *p, const void *q, c
     a.W = pa.W;
     a.m = pa.compress_rate;
     a.scale = pa.scale;
-    a.n_chunks = (pa.S + csa::kBwdChunkRows - 1) / csa::kBwdChunkRows;
-    a.n_jtiles = (pa.W + csa::kBwdKeyTile - 1) / csa::kBwdKeyTile;
-    a.n_blk = (pa.W + 31) / 32;
+    a.n_chunks = (int)(((int64_t)pa.S + csa::kBwdChunkRows - 1) / csa::kBwdChunkRows);
+    a.n_jtiles = (int)(((int64_t)pa.W + csa::kBwdKeyTile - 1) / csa::kBwdKeyTile);
+    a.n_blk = (int)(((int64_t)pa.W + 31) / 32);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = csa::launch_bwd_rows(pa.D, c.HB, a, s);
     if (e != hipSuccess)
