@@ -59,30 +59,45 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 CSRC = os.path.join(ROOT, "sparse_attention_indexer_csa_amd", "csrc")
 CALIB_LIB = os.path.join(ROOT, "sparse_attention_indexer_csa_amd", "libcsa_calib.so")
 
-# HBM bytes per launch of the fused prefill kernel, from FETCH_SIZE and
-# WRITE_SIZE counter runs scaled by what the same counters read for a plain
-# copy of known size.  Valid only for the kernel sources they were taken on
-# (sha256 over the files the forward kernels are compiled from); reported as
-# null otherwise.
-MEASURED_TRAFFIC = None
-
+# HBM bytes per call, from FETCH_SIZE and WRITE_SIZE counter runs scaled by
+# what the same counters read for the calibration copy of 1 GiB (FETCH_SIZE
+# x 1.99996, WRITE_SIZE x 1.0), summed over the kernels of the call.  Each
+# entry is valid only for the kernel sources it was taken on (sha256 over the
+# files its kernels are compiled from); reported as null otherwise.
 FORWARD_SOURCES = ["csa_device.hpp", "csa_kernels.hip", "csa_launch.hpp", "csa_score.hpp", "csa_topk.hpp"]
+BACKWARD_SOURCES = ["csa_backward.hip", "csa_backward.hpp", "csa_device.hpp", "csa_score.hpp"]
+MEASURED_TRAFFIC = {
+    "select": {"sources": FORWARD_SOURCES,
+               "sha": "de2ae83cf8a15e038360c52da01c43e945eede73607e8d4aa1285e00b75aa55b",
+               "kernels": ["rows3_kernel<128, 2, 2>"], "fetch_bytes": 289764029, "write_bytes": 33554524},
+    "decode": {"sources": FORWARD_SOURCES,
+               "sha": "de2ae83cf8a15e038360c52da01c43e945eede73607e8d4aa1285e00b75aa55b",
+               "kernels": ["stream_kernel<128, 2>", "topk_block_kernel"], "fetch_bytes": 326206557,
+               "write_bytes": 5109963},
+    "backward": {"sources": BACKWARD_SOURCES,
+                 "sha": "58e4470befbf3d5c02dada0f1d25e9c9ca9ed584995f5f1a29cd3410e0f3edb6",
+                 "kernels": ["bwd_rows_kernel<128, 2>", "bwd_keys_kernel<128, 2>", "bwd_reduce_kernel"],
+                 "fetch_bytes": 1365779082, "write_bytes": 882802435},
+}
+
 DEFAULT_LEGS = "calib,select,score,packed,decode,backward,kl,cpu"
 
 
-def sources_sha():
+def sources_sha(names=FORWARD_SOURCES):
     h = hashlib.sha256()
-    for name in sorted(FORWARD_SOURCES):
+    for name in sorted(names):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    t = MEASURED_TRAFFIC
-    if t is None or t["sources_sha"] != sources_sha():
+def measured_traffic(leg):
+    """HBM bytes per call of the leg's kernels (fetch + write), or None when
+    the counters were taken on other kernel sources."""
+    t = MEASURED_TRAFFIC.get(leg)
+    if t is None or t["sha"] != sources_sha(t["sources"]):
         return None
-    return t["bytes_per_launch"]
+    return t["fetch_bytes"] + t["write_bytes"]
 
 
 def row_kernel_name(P):
@@ -291,7 +306,7 @@ def main():
         result["ms_per_step"] = t["wall_ms"]
         achieved = flops / (t["ev_mean"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic("select"),
                 "kernel": row_kernel_name(P), "kernel_ms_mean": t["ev_mean"], "kernel_ms_median": t["ev_median"],
                 "kernel_ms_min": t["ev_min"], "flops_per_launch": flops, "sources_sha": sources_sha()[:16]}
         if achievable:
@@ -354,7 +369,8 @@ def main():
                               "entries_per_s": pairs / (t["wall_ms"] * 1e-3), "ms_per_step": t["wall_ms"],
                               "call_ms_mean": t["ev_mean"], "call_ms_median": t["ev_median"],
                               "call_ms_min": t["ev_min"], "flops_per_call": bflops, "tflops": ach,
-                              "mfma_frac": ach / PEAK_BF16_TFLOPS, "workspace_bytes": wsb.numel()}
+                              "mfma_frac": ach / PEAK_BF16_TFLOPS, "workspace_bytes": wsb.numel(),
+                              "traffic": measured_traffic("backward")}
         log(f"backward: {t['wall_ms']:.3f} ms/step, call {t['ev_mean']:.3f} ms, {ach:.1f} TFLOP/s")
         del g, dq, dk, dw, wsb
 
@@ -401,7 +417,8 @@ def main():
         dec = {"workload": CONFIG_TITLES["c5"], "rows_per_s": Pd.B / (t["wall_ms"] * 1e-3),
                "ms_per_step": t["wall_ms"], "call_ms_mean": t["ev_mean"], "call_ms_median": t["ev_median"],
                "call_ms_min": t["ev_min"], "algorithmic_bytes": alg_bytes, "GB_s": gbs,
-               "hbm_frac": gbs / PEAK_HBM_GBS, "plan": csa.resolve_plan(dd["q"], dd["k"], dd["w"], Pd.m)}
+               "hbm_frac": gbs / PEAK_HBM_GBS, "plan": csa.resolve_plan(dd["q"], dd["k"], dd["w"], Pd.m),
+               "traffic": measured_traffic("decode")}
         if achievable:
             dec["hbm_frac_of_achievable_read"] = gbs / achievable["hbm_read_GBs"]
         result["decode"] = dec
@@ -419,7 +436,7 @@ def main():
         oracle.select(P, rows)
         dt = time.perf_counter() - t0
         cpu.update(value=sample_pairs / dt, seconds=dt,
-                   sample=f"every {args.cpu_row_stride}th query row of the seq-16384 prefill "
+                   sample=f"one query row in {args.cpu_row_stride} of the seq-16384 prefill "
                           f"({len(rows)} rows, {sample_pairs} causal pairs), scores + top-k")
         Pd = make_config("c5")
         drows = np.arange(0, Pd.B, 4)
