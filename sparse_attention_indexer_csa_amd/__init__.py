@@ -268,15 +268,18 @@ def select(q, k, w, top_k: int, compress_rate: int, scale: float = 1.0, q_offset
     elif out.dtype != torch.int32 or not out.is_contiguous() or tuple(out.shape) != (p.B, p.S, int(top_k)):
         raise ValueError("out must be a contiguous int32 [B,S,top_k] tensor")
     sc = torch.empty((p.B, p.S, p.W), dtype=torch.float32, device=dev) if return_scores else None
-    need = ctypes.c_size_t(0)
-    st = lib.csa_index_workspace_size(ctypes.byref(p), int(top_k), ctypes.byref(need))
-    if st != _OK:
-        _raise(st, "csa_index_workspace_size")
     ws = None
-    if sc is None and need.value > 0:
-        if workspace is not None and workspace.is_cuda and workspace.numel() * workspace.element_size() >= need.value:
-            ws = workspace
-        else:
+    if workspace is not None:
+        # the caller's buffer as is: the library checks its size (no host query per call)
+        if not workspace.is_cuda:
+            raise ValueError("workspace must be a device tensor")
+        ws = workspace
+    elif sc is None:
+        need = ctypes.c_size_t(0)
+        st = lib.csa_index_workspace_size(ctypes.byref(p), int(top_k), ctypes.byref(need))
+        if st != _OK:
+            _raise(st, "csa_index_workspace_size")
+        if need.value > 0:
             ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = lib.csa_index_select(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(w), ctypes.byref(m), int(top_k), _ptr(out),
@@ -379,15 +382,18 @@ def score_backward(q, k, w, grad, compress_rate: int, scale: float = 1.0, q_offs
     dq = out(dq, "dq", (p.B, p.H, p.S, p.D))
     dk = out(dk, "dk", (p.B, p.W, p.D))
     dw = out(dw, "dw", (p.B, p.S, p.H))
-    need = ctypes.c_size_t(0)
-    st = lib.csa_index_backward_workspace_size(ctypes.byref(p), ctypes.byref(need))
-    if st != _OK:
-        _raise(st, "csa_index_backward_workspace_size")
     ws = None
-    if need.value > 0:
-        if workspace is not None and workspace.is_cuda and workspace.numel() * workspace.element_size() >= need.value:
-            ws = workspace
-        else:
+    if workspace is not None:
+        # the caller's buffer as is: the library checks its size (no host query per call)
+        if not workspace.is_cuda:
+            raise ValueError("workspace must be a device tensor")
+        ws = workspace
+    else:
+        need = ctypes.c_size_t(0)
+        st = lib.csa_index_backward_workspace_size(ctypes.byref(p), ctypes.byref(need))
+        if st != _OK:
+            _raise(st, "csa_index_backward_workspace_size")
+        if need.value > 0:
             ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     st = lib.csa_index_score_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(w), ctypes.byref(m), _ptr(grad),
