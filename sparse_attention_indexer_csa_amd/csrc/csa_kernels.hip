@@ -1184,17 +1184,17 @@ __host__ __device__ constexpr size_t topk_block_fast_lds_bytes(int W)
 
 __device__ __forceinline__ bool topk_block_fast(const float *src, int n, int k, unsigned char *smem, int32_t *out)
 {
-    constexpr int NW = kTopkBlockWaves, NT = NW * kWave, kB = 4;
+    constexpr int NW = kTopkBlockWaves, NT = NW * kWave, kB = 16;
     static_assert(2 * kBlockCandMax * 4 <= kCoarseBins * 4, "candidates fit the histogram's place");
     uint32_t *hist = reinterpret_cast<uint32_t *>(smem);
     uint32_t *ckey = hist, *cent = hist + kBlockCandMax;
     uint32_t *row = hist + kCoarseBins;
     const int n4 = (n + 3) / 4;
     int *part = reinterpret_cast<int *>(row + 4 * n4);
-    int *count = part + NW + 1;
-    const int t = threadIdx.x, l = lane();
+    const int t = threadIdx.x, wv = t / kWave;
 
-    // pass 1: the keys to LDS and the coarse histogram
+    // pass 1: the keys to LDS and the coarse histogram; kB loads per thread
+    // in flight (a 32768-entry row is one batch)
     coarse_clear<NW>(hist);
     __syncthreads();
     const bool vec = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
@@ -1202,15 +1202,15 @@ __device__ __forceinline__ bool topk_block_fast(const float *src, int n, int k, 
     const float4 *src4 = reinterpret_cast<const float4 *>(src);
     u32x4 *row4 = reinterpret_cast<u32x4 *>(row);
 #pragma unroll 1
-    for (int i0 = 0; i0 < nv; i0 += 8 * NT) {
-        float4 v[8];
+    for (int i0 = 0; i0 < nv; i0 += kB * NT) {
+        float4 v[kB];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
+        for (int x = 0; x < kB; ++x) {
             const int i = i0 + x * NT + t;
             v[x] = i < nv ? src4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         }
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
+        for (int x = 0; x < kB; ++x) {
             const int i = i0 + x * NT + t;
             const u32x4 kv = {score_key(v[x].x), score_key(v[x].y), score_key(v[x].z), score_key(v[x].w)};
             if (i < nv)
@@ -1230,52 +1230,54 @@ __device__ __forceinline__ bool topk_block_fast(const float *src, int n, int k, 
     // candidates: the keys in (tau, kKeyPosInf]
     const uint32_t tau = coarse_find<NW>(hist, k, part);
     const uint32_t lo = tau + 1u, span = kKeyPosInf - lo;
-    if (t == 0)
-        *count = 0;
-    __syncthreads();
-    // pass 2 over the LDS row: append the candidates (in any order: the sort
-    // orders them), one atomic per wave and batch
-#pragma unroll 1
-    for (int i0 = 0; i0 < n4; i0 += kB * NT) {
-        u32x4 kv[kB];
-        int c = 0;
+    // this thread's keys: blocks i = t + NT x of four keys (entries past n
+    // read as 0, never a candidate)
+    auto block_keys = [&](int i) {
+        u32x4 kv = row4[i];
 #pragma unroll
-        for (int x = 0; x < kB; ++x) {
-            const int i = i0 + x * NT + t;
-            kv[x] = i < n4 ? row4[i] : u32x4{0u, 0u, 0u, 0u};
+        for (int e = 0; e < 4; ++e)
+            if (4 * i + e >= n)
+                kv[e] = 0u;
+        return kv;
+    };
+    // pass 2 over the LDS row: count this thread's candidates, place them by
+    // a workgroup prefix sum, then write them (thread order: the sort orders
+    // them)
+    int c = 0;
+#pragma unroll 4
+    for (int i = t; i < n4; i += NT) {
+        const u32x4 kv = block_keys(i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            c += (kv[e] - lo <= span) ? 1 : 0;
+    }
+    const int incl = wave_inclusive_sum(c);
+    if (lane() == kWave - 1)
+        part[wv] = incl;
+    __syncthreads();
+    int pos = incl - c, m = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        pos += w < wv ? part[w] : 0;
+        m += part[w];
+    }
+    if (m > kBlockCandMax)
+        return false;
+    if (c > 0) {
+#pragma unroll 4
+        for (int i = t; i < n4; i += NT) {
+            const u32x4 kv = block_keys(i);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                if (4 * i + e >= n)
-                    kv[x][e] = 0u; // past the row: never a candidate
-                c += (kv[x][e] - lo <= span) ? 1 : 0;
-            }
-        }
-        const int incl = wave_inclusive_sum(c);
-        const int wave_total = read_lane(incl, kWave - 1);
-        if (wave_total > 0) {
-            int base = 0;
-            if (l == kWave - 1)
-                base = atomicAdd(count, wave_total);
-            int slot = read_lane(base, kWave - 1) + incl - c;
-#pragma unroll
-            for (int x = 0; x < kB; ++x) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (kv[x][e] - lo <= span) {
-                        if (slot < kBlockCandMax) {
-                            ckey[slot] = kv[x][e];
-                            cent[slot] = (uint32_t)(4 * (i0 + x * NT + t) + e);
-                        }
-                        ++slot;
-                    }
+                if (kv[e] - lo <= span) {
+                    ckey[pos] = kv[e];
+                    cent[pos] = (uint32_t)(4 * i + e);
+                    ++pos;
                 }
             }
         }
     }
     __syncthreads();
-    const int m = *count;
-    if (m > kBlockCandMax)
-        return false;
     // the sort buffer takes the row's place: the LDS holds W >= 8192 keys on
     // this path, at least the 16 KB of 2048 composites (it may cover the
     // counters, which are not read again)
