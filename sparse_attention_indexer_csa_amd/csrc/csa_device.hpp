@@ -78,6 +78,14 @@ __device__ __forceinline__ int opaque_lane()
     return l;
 }
 
+// v in an SGPR of its own.  A scalar read from the argument block otherwise
+// shares its register tuple with its neighbours; when register pressure
+// spills the tuple, every use restores all of it.
+__device__ __forceinline__ int own_sgpr(int v)
+{
+    __asm__ volatile("" : "+s"(v));
+    return v;
+}
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ uint32_t uniform_u(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
 

@@ -389,6 +389,7 @@ void rows3_kernel(const KernelArgs a)
     const int wv = uniform(tid / kWave);
     const int l = lane();
 
+    const int W = own_sgpr(a.W), top_k = own_sgpr(a.top_k), cap = own_sgpr(a.cap);
     const int rb = a.n_row_blocks - 1 - (int)(blockIdx.x / a.B);
     const int b = (int)(blockIdx.x % a.B);
     const int row0 = rb * kRowsPerBlock;
@@ -397,12 +398,12 @@ void rows3_kernel(const KernelArgs a)
 
     const int64_t off = a.q_offset ? (int64_t)a.q_offset[b] : 0;
     const int last = min(row0 + kRowsPerBlock, a.S) - 1;
-    const int thr_last = visible_entries(off + last, a.m, a.W);
+    const int thr_last = visible_entries(off + last, a.m, W);
     const int nunits = (thr_last + kTileEntries - 1) / kTileEntries; // 64-entry units
     const int ntiles = (thr_last + kTile3 - 1) / kTile3;             // 32-entry tiles
-    const int thr = active ? visible_entries(off + i, a.m, a.W) : 0;
+    const int thr = active ? visible_entries(off + i, a.m, W) : 0;
     const int qseg = (a.q_seg && active) ? a.q_seg[(int64_t)b * a.S + i] : 0;
-    const int32_t *kseg = a.k_seg ? a.k_seg + (int64_t)b * a.W : nullptr;
+    const int32_t *kseg = a.k_seg ? a.k_seg + (int64_t)b * W : nullptr;
     const int64_t row_id = (int64_t)b * a.S + i;
 
     // With segments, units before the first one that holds an entry of any
@@ -410,7 +411,7 @@ void rows3_kernel(const KernelArgs a)
     int u_lo = 0;
     if (kseg) {
         __shared__ int first_unit[kRowWaves];
-        const int fu = active ? first_segment_unit(kseg, thr, qseg, nunits, a.W) : nunits;
+        const int fu = active ? first_segment_unit(kseg, thr, qseg, nunits, W) : nunits;
         if (l == 0)
             first_unit[wv] = fu;
         __syncthreads();
@@ -421,10 +422,10 @@ void rows3_kernel(const KernelArgs a)
 
     TopKRow<uint16_t> tk;
     if (MODE & kModeSelect) {
-        unsigned char *base = smem + 2 * G::kBufBytes + (size_t)wv * rows_topk_wave_bytes(a.cap);
+        unsigned char *base = smem + 2 * G::kBufBytes + (size_t)wv * rows_topk_wave_bytes(cap);
         uint32_t *hist = reinterpret_cast<uint32_t *>(base);
         uint32_t *key = hist + 256;
-        topk_init(tk, key, reinterpret_cast<uint16_t *>(key + a.cap + kWave), hist, a.cap, a.top_k);
+        topk_init(tk, key, reinterpret_cast<uint16_t *>(key + cap + kWave), hist, cap, top_k);
     }
 
     // Key tiles by DMA, as in rows_kernel: DMA instruction o of a tile writes
@@ -433,7 +434,6 @@ void rows3_kernel(const KernelArgs a)
     const uint16_t *kb = a.k + b * a.k_sb;
     const int entry_bytes = (int)a.k_sw * 2;
     const int64_t tile_stride = (int64_t)kTile3 * a.k_sw;
-    const int W = a.W;
     uint32_t dma_off[G::kDmaPerWave];
 #pragma unroll
     for (int x = 0; x < G::kDmaPerWave; ++x) {
@@ -451,15 +451,15 @@ void rows3_kernel(const KernelArgs a)
     };
 
     KLAcc klacc = kl_empty();
-    const float *tgt_row = (MODE & kModeKL) && active ? a.target + row_id * a.W : nullptr;
+    const float *tgt_row = (MODE & kModeKL) && active ? a.target + row_id * W : nullptr;
     auto tgt_load = [&](int u) -> float {
         if (!(MODE & kModeKL) || !active)
             return 0.0f;
-        return tgt_row[min(u * kTileEntries + l, a.W - 1)];
+        return tgt_row[min(u * kTileEntries + l, W - 1)];
     };
     // segment id of this lane's entry of unit u (loaded at the unit's first
     // tile, compared at its last, so the load's latency is hidden)
-    auto seg_load = [&](int u) -> int { return kseg ? kseg[min(u * kTileEntries + l, a.W - 1)] : 0; };
+    auto seg_load = [&](int u) -> int { return kseg ? kseg[min(u * kTileEntries + l, W - 1)] : 0; };
     auto unit_valid = [&](int u, int seg) {
         const int j = u * kTileEntries + l;
         bool v = j < thr;
@@ -471,8 +471,8 @@ void rows3_kernel(const KernelArgs a)
         const int j = u * kTileEntries + l;
         const float outv = valid ? s : -INFINITY;
         if (MODE & kModeScores) {
-            if (j < a.W)
-                a.scores[row_id * a.W + j] = outv;
+            if (j < W)
+                a.scores[row_id * W + j] = outv;
         }
         if (MODE & kModeSelect)
             topk_push_unchecked(tk, score_key(outv), (uint32_t)j, valid);
@@ -541,16 +541,16 @@ void rows3_kernel(const KernelArgs a)
         return;
     if (MODE & kModeScores) {
         // entries before the first computed unit and past the last are masked
-        for (int j = l; j < min(u_lo * kTileEntries, a.W); j += kWave)
-            a.scores[row_id * a.W + j] = -INFINITY;
-        for (int j = max(nunits, u_lo) * kTileEntries + l; j < a.W; j += kWave)
-            a.scores[row_id * a.W + j] = -INFINITY;
+        for (int j = l; j < min(u_lo * kTileEntries, W); j += kWave)
+            a.scores[row_id * W + j] = -INFINITY;
+        for (int j = max(nunits, u_lo) * kTileEntries + l; j < W; j += kWave)
+            a.scores[row_id * W + j] = -INFINITY;
     }
     if (MODE & kModeSelect) {
-        if (a.cap <= 24 * kWave)
-            topk_finish_regs<24>(tk, a.idx + row_id * a.top_k);
+        if (cap <= 24 * kWave)
+            topk_finish_regs<24>(tk, a.idx + row_id * top_k);
         else
-            topk_finish(tk, a.idx + row_id * a.top_k);
+            topk_finish(tk, a.idx + row_id * top_k);
     }
     if (MODE & kModeKL) {
         const KLAcc tot = kl_wave_reduce(klacc);

@@ -105,14 +105,28 @@ __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v)
     }
 }
 
-// Smallest and largest key of key[0..count), count >= 1.
+// The buffer passes below read the keys in batches of kPassBatch chunks of 64
+// (the reads of a batch are in flight together, indexes past the end clamped
+// to the last key) instead of one dependent read per chunk.
+constexpr int kPassBatch = 4;
+
+// Smallest and largest key of key[0..count), count >= 1.  (A clamped
+// duplicate of the last key changes neither.)
 __device__ __forceinline__ void key_range(const uint32_t *key, int count, uint32_t &lo, uint32_t &hi)
 {
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-    for (int i = lane(); i < count; i += kWave) {
-        const uint32_t kv = key[i];
-        mn = min(mn, kv);
-        mx = max(mx, kv);
+    const int l = lane();
+#pragma unroll 1
+    for (int b0 = 0; b0 < count; b0 += kPassBatch * kWave) {
+        uint32_t kv[kPassBatch];
+#pragma unroll
+        for (int c = 0; c < kPassBatch; ++c)
+            kv[c] = key[min(b0 + c * kWave + l, count - 1)];
+#pragma unroll
+        for (int c = 0; c < kPassBatch; ++c) {
+            mn = min(mn, kv[c]);
+            mx = max(mx, kv[c]);
+        }
     }
     mn = min(mn, lane_xor_u32<1>(mn));
     mx = max(mx, lane_xor_u32<1>(mx));
@@ -138,10 +152,19 @@ __device__ __forceinline__ int bucket_of_kth(const uint32_t *key, int count, uin
     for (int b = lane(); b < 256; b += kWave)
         hist[b] = 0u;
     wave_lds_fence();
-    for (int i = lane(); i < count; i += kWave) {
-        const uint32_t off = key[i] - base;
-        if (off <= span)
-            atomicAdd(&hist[off >> shift], 1u);
+    const int l = lane();
+#pragma unroll 1
+    for (int b0 = 0; b0 < count; b0 += kPassBatch * kWave) {
+        uint32_t kv[kPassBatch];
+#pragma unroll
+        for (int c = 0; c < kPassBatch; ++c)
+            kv[c] = key[min(b0 + c * kWave + l, count - 1)];
+#pragma unroll
+        for (int c = 0; c < kPassBatch; ++c) {
+            const uint32_t off = kv[c] - base;
+            if (b0 + c * kWave + l < count && off <= span)
+                atomicAdd(&hist[off >> shift], 1u);
+        }
     }
     wave_lds_fence();
     const int d = find_digit(hist, kk, above);
@@ -235,28 +258,39 @@ __device__ __forceinline__ void radix_select(const uint32_t *key, int count, int
 }
 
 // Keep keys > T and the first ties_keep keys == T, in place and in order.
-// Returns the new count.
+// Returns the new count.  A batch is read before any of it is written: the
+// kept pairs of a chunk land at or below the chunk's own positions, so no
+// write reaches a pair not yet read.
 template <typename EntT>
 __device__ __forceinline__ int compact_keep(uint32_t *key, EntT *ent, int count, uint32_t T, int ties_keep)
 {
     int out = 0, ties = 0;
+    const int l = lane();
 #pragma unroll 1
-    for (int base = 0; base < count; base += kWave) {
-        const int i = base + lane();
-        const bool in = i < count;
-        const uint32_t kv = in ? key[i] : 0u;
-        const EntT ev = in ? ent[i] : (EntT)0;
-        const bool eq = in && kv == T;
-        const uint64_t beq = ballot(eq);
-        const bool keep = (in && kv > T) || (eq && ties + rank_below(beq) < ties_keep);
-        ties += popc64(beq);
-        const uint64_t bk = ballot(keep);
-        if (keep) {
-            const int pos = out + rank_below(bk);
-            key[pos] = kv;
-            ent[pos] = ev;
+    for (int b0 = 0; b0 < count; b0 += kPassBatch * kWave) {
+        uint32_t kv[kPassBatch];
+        EntT ev[kPassBatch];
+#pragma unroll
+        for (int c = 0; c < kPassBatch; ++c) {
+            const int i = min(b0 + c * kWave + l, count - 1);
+            kv[c] = key[i];
+            ev[c] = ent[i];
         }
-        out += popc64(bk);
+#pragma unroll
+        for (int c = 0; c < kPassBatch; ++c) {
+            const bool in = b0 + c * kWave + l < count;
+            const bool eq = in && kv[c] == T;
+            const uint64_t beq = ballot(eq);
+            const bool keep = (in && kv[c] > T) || (eq && ties + rank_below(beq) < ties_keep);
+            ties += popc64(beq);
+            const uint64_t bk = ballot(keep);
+            if (keep) {
+                const int pos = out + rank_below(bk);
+                key[pos] = kv[c];
+                ent[pos] = ev[c];
+            }
+            out += popc64(bk);
+        }
     }
     wave_lds_fence();
     return out;
@@ -614,9 +648,11 @@ __device__ __forceinline__ uint32_t from_next_lane(uint32_t v)
 }
 
 // Returns false (and writes nothing) when the truncated composites cannot
-// order the buffer exactly.
-template <int E, typename EntT>
-__device__ __forceinline__ bool sort_and_write_fast(const uint32_t *key, const EntT *ent, int n, int k, int32_t *out)
+// order the buffer exactly.  With kRange the caller passes bounds lo <= every
+// key <= hi of key[0..n) (wave-uniform) instead of having them reduced here.
+template <int E, typename EntT, bool kRange = false>
+__device__ __forceinline__ bool sort_and_write_fast(const uint32_t *key, const EntT *ent, int n, int k, int32_t *out,
+                                                    uint32_t lo = 0u, uint32_t hi = 0u)
 {
     constexpr int PB = (E == 1) ? 6 : (E == 2) ? 7 : (E == 4) ? 8 : 9;
     static_assert((kWave * E) == (1 << PB), "position bits");
@@ -631,19 +667,23 @@ __device__ __forceinline__ bool sort_and_write_fast(const uint32_t *key, const E
         mn = e < n ? min(mn, kr[r]) : mn;
         mx = max(mx, kr[r]);
     }
-    mn = min(mn, lane_xor_u32<1>(mn));
-    mx = max(mx, lane_xor_u32<1>(mx));
-    mn = min(mn, lane_xor_u32<2>(mn));
-    mx = max(mx, lane_xor_u32<2>(mx));
-    mn = min(mn, lane_xor_u32<4>(mn));
-    mx = max(mx, lane_xor_u32<4>(mx));
-    mn = min(mn, lane_xor_u32<8>(mn));
-    mx = max(mx, lane_xor_u32<8>(mx));
-    mn = min(mn, lane_xor_u32<16>(mn));
-    mx = max(mx, lane_xor_u32<16>(mx));
-    mn = min(mn, lane_xor_u32<32>(mn));
-    mx = max(mx, lane_xor_u32<32>(mx));
-    const uint32_t kmin = uniform_u(mn), span = uniform_u(mx) - kmin;
+    uint32_t kmin = lo, span = hi - lo;
+    if constexpr (!kRange) {
+        mn = min(mn, lane_xor_u32<1>(mn));
+        mx = max(mx, lane_xor_u32<1>(mx));
+        mn = min(mn, lane_xor_u32<2>(mn));
+        mx = max(mx, lane_xor_u32<2>(mx));
+        mn = min(mn, lane_xor_u32<4>(mn));
+        mx = max(mx, lane_xor_u32<4>(mx));
+        mn = min(mn, lane_xor_u32<8>(mn));
+        mx = max(mx, lane_xor_u32<8>(mx));
+        mn = min(mn, lane_xor_u32<16>(mn));
+        mx = max(mx, lane_xor_u32<16>(mx));
+        mn = min(mn, lane_xor_u32<32>(mn));
+        mx = max(mx, lane_xor_u32<32>(mx));
+        kmin = uniform_u(mn);
+        span = uniform_u(mx) - kmin;
+    }
     const int bits = span ? 32 - __builtin_clz(span) : 0;
     const int shift = bits > 32 - PB ? bits - (32 - PB) : 0;
     uint32_t c[E];
@@ -681,6 +721,32 @@ __device__ __forceinline__ bool sort_and_write_fast(const uint32_t *key, const E
     for (int e = kWave * E + l; e < k; e += kWave)
         out[e] = -1;
     return true;
+}
+
+// sort_pairs_and_write for n pairs whose keys all lie in [lo, hi]
+// (wave-uniform bounds known to the caller).
+template <typename EntT>
+__device__ __forceinline__ void sort_pairs_in_range_and_write(const uint32_t *key, const EntT *ent, int n, int k,
+                                                              int32_t *out, uint32_t lo, uint32_t hi)
+{
+    wave_lds_fence();
+    if (n <= 64) {
+        if (!sort_and_write_fast<1, EntT, true>(key, ent, n, k, out, lo, hi))
+            sort_and_write<1, EntT>(key, ent, n, k, out);
+    } else if (n <= 128) {
+        if (!sort_and_write_fast<2, EntT, true>(key, ent, n, k, out, lo, hi))
+            sort_and_write<2, EntT>(key, ent, n, k, out);
+    } else if (n <= 256) {
+        if (!sort_and_write_fast<4, EntT, true>(key, ent, n, k, out, lo, hi))
+            sort_and_write<4, EntT>(key, ent, n, k, out);
+    } else if (n <= 512) {
+        if (!sort_and_write_fast<8, EntT, true>(key, ent, n, k, out, lo, hi))
+            sort_and_write<8, EntT>(key, ent, n, k, out);
+    } else if (n <= 1024) {
+        sort_and_write<16, EntT>(key, ent, n, k, out);
+    } else {
+        sort_and_write<32, EntT>(key, ent, n, k, out);
+    }
 }
 
 template <typename EntT>
@@ -727,8 +793,9 @@ __device__ __forceinline__ int bucket_of_kth_regs(const uint32_t (&kr)[NR], uint
     wave_lds_fence();
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
+        // an empty slot (0) wraps to 0 - base > span: base >= 1
         const uint32_t off = kr[r] - base;
-        if (kr[r] != 0u && off <= span)
+        if (off <= span)
             atomicAdd(&hist[off >> shift], 1u);
     }
     wave_lds_fence();
@@ -787,7 +854,8 @@ __device__ __forceinline__ void topk_finish_regs(TopKRow<EntT> &t, int32_t *out)
     mx = max(mx, lane_xor_u32<16>(mx));
     mn = min(mn, lane_xor_u32<32>(mn));
     mx = max(mx, lane_xor_u32<32>(mx));
-    uint32_t base = uniform_u(mn), span = uniform_u(mx) - base;
+    const uint32_t kmax = uniform_u(mx);
+    uint32_t base = uniform_u(mn), span = kmax - base;
     int kk = k;
     uint32_t T = base;
     int ties_keep = 0;
@@ -808,11 +876,11 @@ __device__ __forceinline__ void topk_finish_regs(TopKRow<EntT> &t, int32_t *out)
             int cnt = 0;
 #pragma unroll
             for (int r = 0; r < NR; ++r)
-                cnt += (kr[r] != 0u && kr[r] - base <= span) ? 1 : 0;
+                cnt += (kr[r] - base <= span) ? 1 : 0;
             int pos = wave_exclusive_sum(cnt);
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
-                if (kr[r] != 0u && kr[r] - base <= span)
+                if (kr[r] - base <= span)
                     t.hist[pos++] = kr[r];
             }
             wave_lds_fence();
@@ -829,41 +897,51 @@ __device__ __forceinline__ void topk_finish_regs(TopKRow<EntT> &t, int32_t *out)
         T = base;
         ties_keep = kk;
     }
-    // winners: keys > T at [0, k - ties_keep), the earliest ties after them
-    // (T is a buffered key, so no empty slot (0) compares equal to it)
-    const int n_gt = k - ties_keep;
+    // winners: keys > T and the first ties_keep keys == T, placed at the
+    // front in buffer order.  Slot c of lane l in group m is buffer entry
+    // 256m + 4l + c, so within a group the pairs of lower lanes come first
+    // (counted from four ballots), then this lane's in c order.
     int g_base = 0, e_base = 0;
 #pragma unroll
     for (int m = 0; m < NR / 4; ++m) {
-        int gc = 0, ec = 0;
+        uint64_t beq[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            beq[c] = ballot(kr[4 * m + c] == T);
+        int e = e_base;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            e += rank_below(beq[c]);
+        bool win[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            gc += kr[4 * m + c] > T ? 1 : 0;
-            ec += kr[4 * m + c] == T ? 1 : 0;
+            const uint32_t x = kr[4 * m + c];
+            win[c] = x > T || (x == T && e < ties_keep);
+            e += x == T ? 1 : 0;
         }
-        const int gi = wave_inclusive_sum(gc), ei = wave_inclusive_sum(ec);
-        int gp = g_base + gi - gc, ep = e_base + ei - ec;
+        uint64_t bw[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            bw[c] = ballot(win[c]);
+        int p = g_base;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            p += rank_below(bw[c]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int r = 4 * m + c;
-            if (kr[r] > T) {
-                t.key[gp] = kr[r];
-                t.ent[gp] = er[r];
-                ++gp;
-            } else if (kr[r] == T) {
-                if (ep < ties_keep) {
-                    t.key[n_gt + ep] = kr[r];
-                    t.ent[n_gt + ep] = er[r];
-                }
-                ++ep;
+            if (win[c]) {
+                t.key[p] = kr[r];
+                t.ent[p] = er[r];
+                ++p;
             }
         }
-        g_base += read_lane(gi, kWave - 1);
-        e_base += read_lane(ei, kWave - 1);
+        g_base += popc64(bw[0]) + popc64(bw[1]) + popc64(bw[2]) + popc64(bw[3]);
+        e_base += popc64(beq[0]) + popc64(beq[1]) + popc64(beq[2]) + popc64(beq[3]);
     }
     t.count = k;
     t.tau = T;
-    sort_pairs_and_write(t.key, t.ent, k, k, out);
+    sort_pairs_in_range_and_write(t.key, t.ent, k, k, out, T, kmax);
 }
 
 // ---------------------------------------------------------------------------
