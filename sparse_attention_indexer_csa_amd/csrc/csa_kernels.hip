@@ -402,14 +402,15 @@ void rows3_kernel(const KernelArgs a)
     const int nunits = (thr_last + kTileEntries - 1) / kTileEntries; // 64-entry units
     const int ntiles = (thr_last + kTile3 - 1) / kTile3;             // 32-entry tiles
     const int thr = active ? visible_entries(off + i, a.m, W) : 0;
-    const int qseg = (a.q_seg && active) ? a.q_seg[(int64_t)b * a.S + i] : 0;
-    const int32_t *kseg = a.k_seg ? a.k_seg + (int64_t)b * W : nullptr;
+    constexpr bool kSegs = (MODE & kModeSegs) != 0;
+    const int qseg = (kSegs && active) ? a.q_seg[(int64_t)b * a.S + i] : 0;
+    const int32_t *kseg = kSegs ? a.k_seg + (int64_t)b * W : nullptr;
     const int64_t row_id = (int64_t)b * a.S + i;
 
     // With segments, units before the first one that holds an entry of any
     // row's segment are masked for the whole workgroup and are skipped.
     int u_lo = 0;
-    if (kseg) {
+    if (kSegs) {
         __shared__ int first_unit[kRowWaves];
         const int fu = active ? first_segment_unit(kseg, thr, qseg, nunits, W) : nunits;
         if (l == 0)
@@ -459,11 +460,11 @@ void rows3_kernel(const KernelArgs a)
     };
     // segment id of this lane's entry of unit u (loaded at the unit's first
     // tile, compared at its last, so the load's latency is hidden)
-    auto seg_load = [&](int u) -> int { return kseg ? kseg[min(u * kTileEntries + l, W - 1)] : 0; };
+    auto seg_load = [&](int u) -> int { return kSegs ? kseg[min(u * kTileEntries + l, W - 1)] : 0; };
     auto unit_valid = [&](int u, int seg) {
         const int j = u * kTileEntries + l;
         bool v = j < thr;
-        if (kseg)
+        if (kSegs)
             v = v && seg == qseg;
         return v;
     };
@@ -474,8 +475,9 @@ void rows3_kernel(const KernelArgs a)
             if (j < W)
                 a.scores[row_id * W + j] = outv;
         }
+        // a masked entry carries the key of -inf, which never exceeds tau
         if (MODE & kModeSelect)
-            topk_push_unchecked(tk, score_key(outv), (uint32_t)j, valid);
+            topk_push_unchecked(tk, score_key(outv), (uint32_t)j, true);
         if (MODE & kModeKL) {
             if (valid)
                 kl_add(klacc, s, tgt);
@@ -1459,7 +1461,8 @@ static hipError_t launch_rows_t(int mode, const KernelArgs &a, size_t lds, hipSt
 {
     dim3 grid((unsigned)((int64_t)a.B * a.n_row_blocks)), block(kRowWaves * kWave);
     if constexpr (HB <= 2) {
-        switch (mode) {
+        constexpr int G = kModeSegs;
+        switch (mode | (a.k_seg ? G : 0)) {
         case kModeScores:
             return launch(rows3_kernel<D, HB, kModeScores>, grid, block, lds, s, a);
         case kModeSelect:
@@ -1468,6 +1471,14 @@ static hipError_t launch_rows_t(int mode, const KernelArgs &a, size_t lds, hipSt
             return launch(rows3_kernel<D, HB, kModeScores | kModeSelect>, grid, block, lds, s, a);
         case kModeKL:
             return launch(rows3_kernel<D, HB, kModeKL>, grid, block, lds, s, a);
+        case kModeScores | G:
+            return launch(rows3_kernel<D, HB, kModeScores | G>, grid, block, lds, s, a);
+        case kModeSelect | G:
+            return launch(rows3_kernel<D, HB, kModeSelect | G>, grid, block, lds, s, a);
+        case kModeScores | kModeSelect | G:
+            return launch(rows3_kernel<D, HB, kModeScores | kModeSelect | G>, grid, block, lds, s, a);
+        case kModeKL | G:
+            return launch(rows3_kernel<D, HB, kModeKL | G>, grid, block, lds, s, a);
         default:
             return hipErrorInvalidValue;
         }

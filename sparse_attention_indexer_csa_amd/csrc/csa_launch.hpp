@@ -50,6 +50,9 @@ constexpr int kTopkBlockWaves = 8;
 constexpr int kTopkBlockMinLen = 8192;
 
 enum { kModeScores = 1, kModeSelect = 2, kModeKL = 4 };
+// Added by the row-tile launcher when the call has document segments, so the
+// kernels without them carry no segment code.
+constexpr int kModeSegs = 8;
 
 // Candidate-buffer capacity of the streaming top-k for a given k (room for at
 // least one more 64-pair push after a compaction down to k).  The row-tile
@@ -63,8 +66,7 @@ __host__ __device__ constexpr int rows_topk_capacity(int k, int HB)
     return ((k + 63) / 64) * 64 + (HB <= 2 ? 704 : 1024);
 }
 // LDS bytes of one wave's row-tile buffer: histogram, keys, 16-bit entries,
-// each array with 64 slots past cap for the lanes of a push whose pairs do
-// not enter (topk_push_unchecked).
+// each array with 64 slots past cap.
 __host__ __device__ constexpr size_t rows_topk_wave_bytes(int cap) { return 1024 + (size_t)(cap + 64) * 6; }
 // Entries of the row-tile plan are stored in 16 bits.
 constexpr int kRowTilesMaxW = 65536;

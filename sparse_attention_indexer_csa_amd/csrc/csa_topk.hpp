@@ -33,7 +33,7 @@ struct TopKRow {
     int cap;        // >= k + 64
     int k;
     int count;      // wave-uniform
-    uint32_t tau;   // wave-uniform
+    uint32_t tau;   // wave-uniform, never below kKeyNegInf (the key of -inf)
 };
 
 template <typename EntT>
@@ -359,18 +359,18 @@ __device__ __forceinline__ void topk_push(TopKRow<EntT> &t, uint32_t kv, uint32_
     t.count += n;
 }
 
-// The push without a capacity check or branch, for code that keeps
-// count + 64 <= cap itself (topk_reserve): lanes whose pair does not enter
-// write it to their own slot past the buffer (cap + lane), which the buffer
-// must provide (64 slots beyond cap in both arrays).
+// The push without a capacity check, for code that keeps count + 64 <= cap
+// itself (topk_reserve).
 template <typename EntT>
 __device__ __forceinline__ void topk_push_unchecked(TopKRow<EntT> &t, uint32_t kv, uint32_t entry, bool valid)
 {
     const bool pass = valid && kv > t.tau;
     const uint64_t bal = ballot(pass);
-    const int pos = pass ? t.count + rank_below(bal) : t.cap + lane();
-    t.key[pos] = kv;
-    t.ent[pos] = (EntT)entry;
+    if (pass) {
+        const int pos = t.count + rank_below(bal);
+        t.key[pos] = kv;
+        t.ent[pos] = (EntT)entry;
+    }
     t.count += popc64(bal);
 }
 
