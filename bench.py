@@ -68,16 +68,16 @@ FORWARD_SOURCES = ["csa_device.hpp", "csa_kernels.hip", "csa_launch.hpp", "csa_s
 BACKWARD_SOURCES = ["csa_backward.hip", "csa_backward.hpp", "csa_device.hpp", "csa_score.hpp"]
 MEASURED_TRAFFIC = {
     "select": {"sources": FORWARD_SOURCES,
-               "sha": "de2ae83cf8a15e038360c52da01c43e945eede73607e8d4aa1285e00b75aa55b",
-               "kernels": ["rows3_kernel<128, 2, 2>"], "fetch_bytes": 289764029, "write_bytes": 33554524},
+               "sha": "60b0c13c92fe3edf3787568e4cd22ecb553c4ef8efb3f47243e49962cf20a2bf",
+               "kernels": ["rows3_kernel<128, 2, 2>"], "fetch_bytes": 289557706, "write_bytes": 33554534},
     "decode": {"sources": FORWARD_SOURCES,
-               "sha": "de2ae83cf8a15e038360c52da01c43e945eede73607e8d4aa1285e00b75aa55b",
-               "kernels": ["stream_kernel<128, 2>", "topk_block_kernel"], "fetch_bytes": 326206557,
-               "write_bytes": 5109963},
+               "sha": "60b0c13c92fe3edf3787568e4cd22ecb553c4ef8efb3f47243e49962cf20a2bf",
+               "kernels": ["stream_kernel<128, 2>", "topk_block_kernel"], "fetch_bytes": 326260133,
+               "write_bytes": 5109965},
     "backward": {"sources": BACKWARD_SOURCES,
-                 "sha": "58e4470befbf3d5c02dada0f1d25e9c9ca9ed584995f5f1a29cd3410e0f3edb6",
+                 "sha": "a6641da0fc1211a9f65571f0f91389df0c98efd360ade4a6ba970598ba7dde54",
                  "kernels": ["bwd_rows_kernel<128, 2>", "bwd_keys_kernel<128, 2>", "bwd_reduce_kernel"],
-                 "fetch_bytes": 1365779082, "write_bytes": 882802435},
+                 "fetch_bytes": 1364511920, "write_bytes": 882802688},
 }
 
 DEFAULT_LEGS = "calib,select,score,packed,decode,backward,kl,cpu"
