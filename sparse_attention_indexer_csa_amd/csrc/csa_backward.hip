@@ -352,11 +352,23 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 if (n_head_ok)
                     sign_row[(int64_t)(2 * t + hs) * a.H * 2 + gi] = (uint16_t)sbits;
                 const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
-                // B operand: entries 32hs + c_row(0..7, gi) (+16), column 32c + n
+                // B operand: entries 32hs + c_row(0..7, gi) (+16), column 32c + n;
+                // column block c + 1 is read while block c's products run
+                // (kept in that order by scheduling barriers)
+                bf16x8 b0 = load_column_operand<D>(T, kcol, 0, 0), b1 = load_column_operand<D>(T, kcol, 16, 0);
 #pragma unroll
                 for (int c = 0; c < DB; ++c) {
-                    acc[c] = mfma32(a0, load_column_operand<D>(T, kcol, 0, c), acc[c]);
-                    acc[c] = mfma32(a1, load_column_operand<D>(T, kcol, 16, c), acc[c]);
+                    bf16x8 n0 = b0, n1 = b1;
+                    if (c + 1 < DB) {
+                        n0 = load_column_operand<D>(T, kcol, 0, c + 1);
+                        n1 = load_column_operand<D>(T, kcol, 16, c + 1);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc[c] = mfma32(a0, b0, acc[c]);
+                    acc[c] = mfma32(a1, b1, acc[c]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    b0 = n0;
+                    b1 = n1;
                 }
             }
         }
@@ -423,7 +435,7 @@ struct KeyGeom {
     static constexpr size_t kQBytes = (size_t)kHeads * D * 2;
     static constexpr size_t kWBytes = (size_t)kHeads * 4;
     static constexpr size_t kSBytes = (size_t)kSignWords * 4;
-    static constexpr size_t kLdsBytes = 2 * (kQBytes + kWBytes + kSBytes);
+    static constexpr size_t kLdsBytes = 3 * (kQBytes + kWBytes + kSBytes);
 };
 
 // Position, in a sign word, of the bit of entry e (0..31) of its block: the
@@ -436,18 +448,18 @@ __device__ __forceinline__ int sign_bit_of_entry(int e)
 }
 
 template <int D, int HB>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void bwd_keys_kernel(const BwdArgs a)
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(HB == 4 ? 2 : 3))) void bwd_keys_kernel(const BwdArgs a)
 {
     using G = KeyGeom<D, HB>;
     constexpr int DB = D / 32, NH = G::kHeads;
     static_assert(G::kBlocks == kBwdWaves, "one 32-entry block per wave");
     extern __shared__ __attribute__((aligned(16))) unsigned char bwd_smem[];
-    // two buffers each of one row's q block [NH][D] bf16 (swizzled), its
+    // three buffers each of one row's q block [NH][D] bf16 (swizzled), its
     // weights [NH] fp32 and its sign words [kBlocks][NH]
     auto qbuf = [&](int buf) { return reinterpret_cast<uint16_t *>(bwd_smem + buf * G::kQBytes); };
-    auto wbuf = [&](int buf) { return reinterpret_cast<float *>(bwd_smem + 2 * G::kQBytes + buf * G::kWBytes); };
+    auto wbuf = [&](int buf) { return reinterpret_cast<float *>(bwd_smem + 3 * G::kQBytes + buf * G::kWBytes); };
     auto sbuf = [&](int buf) {
-        return reinterpret_cast<uint32_t *>(bwd_smem + 2 * (G::kQBytes + G::kWBytes) + buf * G::kSBytes);
+        return reinterpret_cast<uint32_t *>(bwd_smem + 3 * (G::kQBytes + G::kWBytes) + buf * G::kSBytes);
     };
 
     // Workgroup -> (batch, chunk, key tile).  Workgroups are dealt to the 8
@@ -490,24 +502,27 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         for (int r = 0; r < 16; ++r)
             acc[c][r] = 0.0f;
 
-    // Staging.  The q block and the weights of row i + 1 (shared by every key
-    // tile of the chunk, so mostly L2 hits) are loaded during row i; the sign
-    // words, this lane's gradient and the row's segment id (read once, from
-    // HBM) two rows ahead, in two register slots that alternate with the
-    // parity of the row.  No loaded value is used before the products that
-    // follow its load: the loads are unconditional (clamped addresses) and
-    // what lies outside the problem is zeroed when stored, the weights are
-    // converted when stored, and slot P is read at the top of its row before
-    // the next load into it is issued.  The far loads are issued after the q
+    // Staging, three rows deep.  Row r's q block, weights and sign words sit
+    // in LDS buffer (r - i_lo) % 3 from the end of row r - 2 on, so that while
+    // row i's products run, the A operand of row i + 1's first head block is
+    // built from its buffer.  The q block and the weights of row i + 2
+    // (shared by every key tile of the chunk, so mostly L2 hits) are loaded
+    // during row i; the sign words, this lane's gradient and the row's
+    // segment id (read once, from HBM) three rows ahead, in three register
+    // slots indexed like the buffers.  No loaded value is used before the
+    // products that follow its load: the loads are unconditional (clamped
+    // addresses) and what lies outside the problem is zeroed when stored,
+    // the weights are converted when stored, and a slot is read before the
+    // next load into it is issued.  The far loads are issued after the q
     // block's, so that waiting for the q block leaves them in flight.
     // The row addresses advance by one row's stride per step (wave-uniform
-    // pointer bumps, no 64-bit index products in the loop), and so does the
-    // causal threshold (no division in the loop).
+    // pointer bumps, no 64-bit index products in the loop), and so do the
+    // causal thresholds (no division in the loop).
     u32x4 pre[G::kPerThread]; // a vector type: HIP's uint4 struct is copied through memory
     uint16_t wraw = 0;
-    uint32_t sgn[2][G::kSignPerThread];
-    float gsl[2] = {0.0f, 0.0f};
-    int ssl[2] = {0, 0};
+    uint32_t sgn[3][G::kSignPerThread];
+    float gsl[3] = {0.0f, 0.0f, 0.0f};
+    int ssl[3] = {0, 0, 0};
     const int blk0 = j0 / 32;
     // per-thread offsets within a row (loop invariant)
     int64_t q_off[G::kPerThread];
@@ -559,14 +574,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         if (w_lane)
             wraw = w_row[tid];
     };
-    auto fetch_far = [&](uint32_t (&sp)[G::kSignPerThread], float &gv, int &sv) {
+    auto fetch_far = [&](uint32_t (&sp)[G::kSignPerThread], float &gv, int &sv) CSA_INLINE {
 #pragma unroll
         for (int u = 0; u < G::kSignPerThread; ++u)
             sp[u] = s_row[s_off[u]];
         gv = g_row[g_off];
         sv = *seg_row;
     };
-    auto store = [&](int buf, const uint32_t (&sp)[G::kSignPerThread]) {
+    auto store = [&](int buf, const uint32_t (&sp)[G::kSignPerThread]) CSA_INLINE {
 #pragma unroll
         for (int u = 0; u < G::kPerThread; ++u) {
             const int c = tid + u * kBwdThreads;
@@ -584,83 +599,133 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         if (tid < NH)
             wbuf(buf)[tid] = bf16_to_f32(wraw); // heads past H: 0
     };
-    // causal threshold of row i: clamp(floor((off + i + 1) / m), 0, W),
-    // carried as quotient and remainder
+    // causal threshold of the row after the current one: clamp(floor((off +
+    // r + 1) / m), 0, W), carried as quotient and remainder
     int64_t thr_q = floor_div_pos(off + i_lo + 1, a.m);
     int thr_r = (int)(off + i_lo + 1 - thr_q * a.m);
-
-    // One row: P = (i - i_lo) % 2 selects the LDS buffers and the slot.
-    // Loads: near row i + 1, far row i + 2 (clamped; rows past the chunk are
-    // loaded and never used, so that the waits are the same on every path).
-    auto row_step = [&](int i, auto P_) CSA_INLINE {
-        constexpr int P = decltype(P_)::value;
-        const float g_i = gsl[P];
-        const int s_i = ssl[P];
-        next_near();
-        fetch_q();
-        next_far();
-        fetch_far(sgn[P], gsl[P], ssl[P]);
-        const int thr = (int)min(max(thr_q, (int64_t)0), (int64_t)a.W);
+    auto next_thr = [&]() CSA_INLINE {
+        const int t = (int)min(max(thr_q, (int64_t)0), (int64_t)a.W);
         if (++thr_r == a.m) {
             thr_r = 0;
             ++thr_q;
         }
+        return t;
+    };
+    // whether (r, j) is unmasked for this lane's entry j
+    auto row_ok = [&](int thr, int sv) CSA_INLINE {
         bool ok = j < thr;
         if (a.k_seg)
-            ok = ok && kseg == s_i;
-        const float ge = ok ? g_i : 0.0f;
-        if (wave_has && ballot(ok) != 0) {
-            const uint16_t *Q = qbuf(P);
-            const float *Wt = wbuf(P);
-            const uint32_t *Sg = sbuf(P) + wv * NH;
-            // rolled for two head blocks (fewer live registers), unrolled for four
-            constexpr int kHbUnroll = HB == 4 ? 4 : 1;
-#pragma unroll kHbUnroll
-            for (int hb = 0; hb < HB; ++hb) {
-                const uint16_t *Qh = Q + 32 * hb * D;
-                // A operand of the dk product, lane = entry n, k index r =
-                // head 32hb + c_row(r, gi): g w [l > 0], with the sign of l
-                // as the row pass found it
-                float pf[16];
+            ok = ok && kseg == sv;
+        return ok;
+    };
+    // A operand of the dk product for head block hb of the row in buffer
+    // buf: lane = entry n, k index r = head 32hb + c_row(r, gi), value
+    // g w [l > 0] with the sign of l as the row pass found it
+    auto operand = [&](int buf, int hb, float ge, bf16x8 &a0, bf16x8 &a1) CSA_INLINE {
+        const float *Wt = wbuf(buf);
+        const uint32_t *Sg = sbuf(buf) + wv * NH;
+        float pf[16];
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    // c_row(4 q4 + c, gi) = 8 q4 + 4 gi + c: four consecutive heads
-                    const float4 wq = *reinterpret_cast<const float4 *>(Wt + 32 * hb + 8 * q4 + 4 * gi);
-                    const uint4 sq = *reinterpret_cast<const uint4 *>(Sg + 32 * hb + 8 * q4 + 4 * gi);
-                    const float wr[4] = {wq.x, wq.y, wq.z, wq.w};
-                    const uint32_t sw[4] = {sq.x, sq.y, sq.z, sq.w};
+        for (int q4 = 0; q4 < 4; ++q4) {
+            // c_row(4 q4 + c, gi) = 8 q4 + 4 gi + c: four consecutive heads
+            const float4 wq = *reinterpret_cast<const float4 *>(Wt + 32 * hb + 8 * q4 + 4 * gi);
+            const uint4 sq = *reinterpret_cast<const uint4 *>(Sg + 32 * hb + 8 * q4 + 4 * gi);
+            const float wr[4] = {wq.x, wq.y, wq.z, wq.w};
+            const uint32_t sw[4] = {sq.x, sq.y, sq.z, sq.w};
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        // all ones when the logit is positive, else zero
-                        const int32_t pos = __builtin_amdgcn_sbfe((int32_t)sw[c], sbit, 1);
-                        // rounded to bf16 by operand_from
-                        pf[4 * q4 + c] = __int_as_float(pos & __float_as_int(ge * wr[c]));
-                    }
-                }
-                const bf16x8 a0 = operand_from(pf, 0), a1 = operand_from(pf, 8);
-#pragma unroll
-                for (int c = 0; c < DB; ++c) {
-                    acc[c] = mfma32(a0, load_column_operand<D>(Qh, qcol, 0, c), acc[c]);
-                    acc[c] = mfma32(a1, load_column_operand<D>(Qh, qcol, 16, c), acc[c]);
-                }
+            for (int c = 0; c < 4; ++c) {
+                // all ones when the logit is positive, else zero
+                const int32_t pos = __builtin_amdgcn_sbfe((int32_t)sw[c], sbit, 1);
+                // rounded to bf16 by operand_from
+                pf[4 * q4 + c] = __int_as_float(pos & __float_as_int(ge * wr[c]));
             }
         }
-        store(P ^ 1, sgn[P ^ 1]); // after the last row: stored, never read
+        a0 = operand_from(pf, 0);
+        a1 = operand_from(pf, 8);
+    };
+    // the q operands of column block c + 1 are read while block c's
+    // products run (kept in that order by scheduling barriers)
+    auto product = [&](int buf, int hb, const bf16x8 &a0, const bf16x8 &a1) CSA_INLINE {
+        const uint16_t *Qh = qbuf(buf) + 32 * hb * D;
+        bf16x8 b0 = load_column_operand<D>(Qh, qcol, 0, 0), b1 = load_column_operand<D>(Qh, qcol, 16, 0);
+#pragma unroll
+        for (int c = 0; c < DB; ++c) {
+            bf16x8 n0 = b0, n1 = b1;
+            if (c + 1 < DB) {
+                n0 = load_column_operand<D>(Qh, qcol, 0, c + 1);
+                n1 = load_column_operand<D>(Qh, qcol, 16, c + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            acc[c] = mfma32(a0, b0, acc[c]);
+            acc[c] = mfma32(a1, b1, acc[c]);
+            __builtin_amdgcn_sched_barrier(0);
+            b0 = n0;
+            b1 = n1;
+        }
+    };
+
+    // One row: P = (i - i_lo) % 3 selects the buffers and the slot of row i;
+    // (P + 1) % 3 is row i + 1's, (P + 2) % 3 receives row i + 2.  On entry
+    // nx0, nx1 hold row i's first head-block operand and thr_i its threshold;
+    // on exit they hold row i + 1's.  Rows past the chunk are loaded,
+    // stored and given operands, never multiplied.
+    bf16x8 nx0, nx1;
+    int thr_i;
+    auto row_step = [&](int i, auto P_) CSA_INLINE {
+        constexpr int P = decltype(P_)::value, P1 = (P + 1) % 3, P2 = (P + 2) % 3;
+        const bool ok = row_ok(thr_i, ssl[P]);
+        const float ge = ok ? gsl[P] : 0.0f;
+        const int thr_n = next_thr();
+        const float ge_n = row_ok(thr_n, ssl[P1]) ? gsl[P1] : 0.0f;
+        next_near();
+        fetch_q(); // row i + 2
+        next_far();
+        fetch_far(sgn[P], gsl[P], ssl[P]); // row i + 3
+        // the loads go out first, the next row's operand is built before
+        // the barrier (scheduling barriers keep both where they are)
+        __builtin_amdgcn_sched_barrier(0);
+        if (wave_has && ballot(ok) != 0) {
+            product(P, 0, nx0, nx1);
+            // rolled: fewer live registers
+#pragma unroll 1
+            for (int hb = 1; hb < HB; ++hb) {
+                bf16x8 a0, a1;
+                operand(P, hb, ge, a0, a1);
+                product(P, hb, a0, a1);
+            }
+        }
+        operand(P1, 0, ge_n, nx0, nx1);
+        // consumed here, so the compiler cannot sink the work past the barrier
+        __asm__ volatile("" ::"v"(nx0), "v"(nx1));
+        __builtin_amdgcn_sched_barrier(0);
+        thr_i = thr_n;
+        store(P2, sgn[P2]); // row i + 2 (after the chunk's last row: stored, never read)
         __syncthreads();
     };
 
+    // prologue: rows i_lo and i_lo + 1 stored, far rows i_lo .. i_lo + 2
+    // loaded, row i_lo's first operand built
     fetch_q();
     fetch_far(sgn[0], gsl[0], ssl[0]);
     next_far();
     fetch_far(sgn[1], gsl[1], ssl[1]);
+    next_far();
+    fetch_far(sgn[2], gsl[2], ssl[2]);
     store(0, sgn[0]);
+    next_near();
+    fetch_q();
     // Every load issued so far completes here (see the row pass).
     __builtin_amdgcn_s_waitcnt(0);
+    store(1, sgn[1]);
     __syncthreads();
-    for (int i = i_lo; i < c1; i += 2) {
+    thr_i = next_thr();
+    operand(0, 0, row_ok(thr_i, ssl[0]) ? gsl[0] : 0.0f, nx0, nx1);
+    for (int i = i_lo; i < c1; i += 3) {
         row_step(i, std::integral_constant<int, 0>());
         if (i + 1 < c1)
             row_step(i + 1, std::integral_constant<int, 1>());
+        if (i + 2 < c1)
+            row_step(i + 2, std::integral_constant<int, 2>());
     }
 
     // partial[b, chunk, entry, d]: lane = column 32c + n, register r = entry jw + c_row(r, gi)
