@@ -75,9 +75,9 @@ MEASURED_TRAFFIC = {
                "kernels": ["stream_kernel<128, 2>", "topk_block_kernel"], "fetch_bytes": 326260133,
                "write_bytes": 5109965},
     "backward": {"sources": BACKWARD_SOURCES,
-                 "sha": "a6641da0fc1211a9f65571f0f91389df0c98efd360ade4a6ba970598ba7dde54",
+                 "sha": "7915e853d7801a745109bfe94b31bc0e61f577c433d8ab4dc3a6649e6ff21db0",
                  "kernels": ["bwd_rows_kernel<128, 2>", "bwd_keys_kernel<128, 2>", "bwd_reduce_kernel"],
-                 "fetch_bytes": 1364511920, "write_bytes": 882802688},
+                 "fetch_bytes": 1489510417, "write_bytes": 882802688},
 }
 
 DEFAULT_LEGS = "calib,select,score,packed,decode,backward,kl,cpu"
