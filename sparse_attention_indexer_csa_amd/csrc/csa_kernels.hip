@@ -711,29 +711,31 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_kernel(const Kernel
 // same XCD.
 // ---------------------------------------------------------------------------
 constexpr int kStreamMaxRows = kStreamRows;
+// rows per thread in the workgroup's prefix over rows, and the slots it fills
+constexpr int kStreamPer = (kStreamMaxRows + kStreamWaves * kWave - 1) / (kStreamWaves * kWave);
+constexpr int kStreamSlots = kStreamPer * kStreamWaves * kWave;
+static_assert(kStreamSlots >= kStreamMaxRows, "every row has a slot");
 
 // Two waves per SIMD: without the bound the compiler takes all 256 VGPRs and
-// some accumulation registers besides, which leaves one wave per SIMD and
-// half of the launched workgroups waiting for the other half.
+// some accumulation registers besides, which leaves one wave per SIMD.
 template <int D, int HB>
-__global__ __launch_bounds__(kSplitWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kStreamWaves * kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void stream_kernel(const KernelArgs a)
 {
     using G = SplitGeom<D>;
     constexpr int KS = D / 16;
-    constexpr int kThreads = kSplitWaves * kWave;
-    constexpr int kPer = kStreamMaxRows / kThreads;
-    static_assert(kPer * kThreads == kStreamMaxRows, "rows per thread");
+    constexpr int kPer = kStreamPer;
     extern __shared__ __align__(16) unsigned char smem[];
-    int *pre = reinterpret_cast<int *>(smem + kSplitWaves * G::kWaveBytes); // [kStreamMaxRows + 1]
-    int *thr_of = pre + kStreamMaxRows + 1;                                // [kStreamMaxRows]
-    __shared__ int wsum[kSplitWaves];
+    int *pre = reinterpret_cast<int *>(smem + kStreamWaves * G::kWaveBytes); // [kStreamSlots + 1]
+    int *thr_of = pre + kStreamSlots + 1;                                    // [kStreamSlots]
+    __shared__ int wsum[kStreamWaves];
     const int tid = threadIdx.x;
     const int wv = uniform(tid / kWave);
     const int l = lane();
     const int rows = (int)a.rows;
 
-    // tiles per row and their exclusive prefix (row-major order)
+    // tiles per row and their exclusive prefix (row-major order); slots past
+    // the last row hold the total
     int cnt[kPer], tot = 0;
 #pragma unroll
     for (int r = 0; r < kPer; ++r) {
@@ -753,7 +755,7 @@ void stream_kernel(const KernelArgs a)
     __syncthreads();
     int before = incl - tot, total = 0;
 #pragma unroll
-    for (int w2 = 0; w2 < kSplitWaves; ++w2) {
+    for (int w2 = 0; w2 < kStreamWaves; ++w2) {
         before += w2 < wv ? wsum[w2] : 0;
         total += wsum[w2];
     }
@@ -763,14 +765,19 @@ void stream_kernel(const KernelArgs a)
         before += cnt[r];
     }
     if (tid == 0)
-        pre[kStreamMaxRows] = total;
+        pre[kStreamSlots] = total;
     __syncthreads();
-
     // this wave's range of tiles [t0, t1)
     const int nblk = (int)gridDim.x;
     const int blk = (nblk % 8 == 0) ? (int)(blockIdx.x % 8) * (nblk / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-    const int64_t gw = (int64_t)blk * kSplitWaves + wv, nw = (int64_t)nblk * kSplitWaves;
+    const int64_t gw = (int64_t)blk * kStreamWaves + wv, nw = (int64_t)nblk * kStreamWaves;
     const int t0 = (int)((int64_t)total * gw / nw), t1 = (int)((int64_t)total * (gw + 1) / nw);
+    // Subtiles each wave has left, for the priority balance below (waves w
+    // and w ^ 4 share a SIMD).
+    static_assert(kStreamWaves == 8, "two waves per SIMD");
+    __shared__ int left[kStreamWaves];
+    if (l == 0)
+        left[wv] = 2 * max(t1 - t0, 0);
     if (t0 >= t1)
         return;
     // row holding tile t0: the last row r with pre[r] <= t0 (rows before it
@@ -875,7 +882,17 @@ void stream_kernel(const KernelArgs a)
         }
         bf16x8 bf[KS];
         load_entries_lds<KS>(bf, reinterpret_cast<const uint16_t *>(wbuf + (sub & 1) * G::kBufBytes), 0, G::kPitch);
+        // The two waves of a SIMD (w and w ^ 4) have equal shares, but the
+        // older one wins the issue arbitration and would finish well ahead:
+        // the wave with more subtiles left takes the higher priority.
+        if (l == 0)
+            left[wv] = nsub - sub;
+        const int partner_left = left[wv ^ 4];
         lds_wait();
+        if (nsub - sub > uniform(partner_left))
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
         __asm__ volatile("" ::: "memory");
         if (pend) {
             score_store(pend_out, pend_j0, pend_thr, pend_kseg, pend_qseg, pend_a, pend_b);
@@ -1545,8 +1562,8 @@ hipError_t launch_split(int D, int HB, const KernelArgs &a, hipStream_t s)
 template <int D>
 static hipError_t launch_stream_d(int HB, const KernelArgs &a, int blocks, hipStream_t s)
 {
-    dim3 grid((unsigned)blocks), block(kSplitWaves * kWave);
-    const size_t lds = (size_t)kSplitWaves * SplitGeom<D>::kWaveBytes + (2 * kStreamMaxRows + 1) * sizeof(int);
+    dim3 grid((unsigned)blocks), block(kStreamWaves * kWave);
+    const size_t lds = (size_t)kStreamWaves * SplitGeom<D>::kWaveBytes + (2 * kStreamSlots + 1) * sizeof(int);
     switch (HB) {
     case 1: return launch(stream_kernel<D, 1>, grid, block, lds, s, a);
     case 2: return launch(stream_kernel<D, 2>, grid, block, lds, s, a);

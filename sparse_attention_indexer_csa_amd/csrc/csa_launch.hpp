@@ -40,9 +40,13 @@ constexpr int kTileEntries = 64;        // compressed entries per LDS K tile
 constexpr int kSplitWaves = 4;
 constexpr int kSplitTiles = 4;          // 64-entry tiles per wave
 constexpr int kSplitChunk = kSplitWaves * kSplitTiles * kTileEntries;
-// Balanced split plan: rows it takes, workgroups per compute unit.
+// Balanced split plan: rows it takes, one workgroup of eight waves per
+// compute unit.  (With two four-wave workgroups per compute unit the older
+// one won the issue arbitration throughout, and the younger one's equal
+// share of the tiles ended up to 20 us later.)
 constexpr int kStreamRows = 256;
-constexpr int kStreamBlocksPerCU = 2;
+constexpr int kStreamWaves = 8;
+constexpr int kStreamBlocksPerCU = 1;
 // Top-k kernel geometry: one wave per row, or one workgroup per long row.
 constexpr int kTopkWaves = 4;
 constexpr int kTopkBlockWaves = 8;
