@@ -435,7 +435,10 @@ struct KeyGeom {
     static constexpr size_t kQBytes = (size_t)kHeads * D * 2;
     static constexpr size_t kWBytes = (size_t)kHeads * 4;
     static constexpr size_t kSBytes = (size_t)kSignWords * 4;
-    static constexpr size_t kLdsBytes = 3 * (kQBytes + kWBytes + kSBytes);
+    // Rows staged three deep, except with four head blocks, where three
+    // buffers of the 32 KB q block would leave one workgroup per compute unit.
+    static constexpr int kDeep = HB <= 2 ? 3 : 2;
+    static constexpr size_t kLdsBytes = kDeep * (kQBytes + kWBytes + kSBytes);
 };
 
 // Position, in a sign word, of the bit of entry e (0..31) of its block: the
@@ -454,12 +457,14 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(HB 
     constexpr int DB = D / 32, NH = G::kHeads;
     static_assert(G::kBlocks == kBwdWaves, "one 32-entry block per wave");
     extern __shared__ __attribute__((aligned(16))) unsigned char bwd_smem[];
-    // three buffers each of one row's q block [NH][D] bf16 (swizzled), its
+    // kDeep buffers each of one row's q block [NH][D] bf16 (swizzled), its
     // weights [NH] fp32 and its sign words [kBlocks][NH]
     auto qbuf = [&](int buf) { return reinterpret_cast<uint16_t *>(bwd_smem + buf * G::kQBytes); };
-    auto wbuf = [&](int buf) { return reinterpret_cast<float *>(bwd_smem + 3 * G::kQBytes + buf * G::kWBytes); };
+    auto wbuf = [&](int buf) {
+        return reinterpret_cast<float *>(bwd_smem + G::kDeep * G::kQBytes + buf * G::kWBytes);
+    };
     auto sbuf = [&](int buf) {
-        return reinterpret_cast<uint32_t *>(bwd_smem + 3 * (G::kQBytes + G::kWBytes) + buf * G::kSBytes);
+        return reinterpret_cast<uint32_t *>(bwd_smem + G::kDeep * (G::kQBytes + G::kWBytes) + buf * G::kSBytes);
     };
 
     // Workgroup -> (batch, chunk, key tile).  Workgroups are dealt to the 8
@@ -703,6 +708,45 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(HB 
         __syncthreads();
     };
 
+    // Two deep (four head blocks): row i's buffer and slot P = (i - i_lo) % 2;
+    // the q block of row i + 1 is loaded and stored during row i, its far
+    // values two rows ahead, and each head block's operand is built in turn.
+    auto row_step2 = [&](int i, auto P_) CSA_INLINE {
+        constexpr int P = decltype(P_)::value, P1 = P ^ 1;
+        const bool ok = row_ok(thr_i, ssl[P]);
+        const float ge = ok ? gsl[P] : 0.0f;
+        thr_i = next_thr();
+        next_near();
+        fetch_q(); // row i + 1
+        next_far();
+        fetch_far(sgn[P], gsl[P], ssl[P]); // row i + 2
+        if (wave_has && ballot(ok) != 0) {
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+                bf16x8 a0, a1;
+                operand(P, hb, ge, a0, a1);
+                product(P, hb, a0, a1);
+            }
+        }
+        store(P1, sgn[P1]); // row i + 1 (after the chunk's last row: stored, never read)
+        __syncthreads();
+    };
+    if constexpr (G::kDeep == 2) {
+        fetch_q();
+        fetch_far(sgn[0], gsl[0], ssl[0]);
+        next_far();
+        fetch_far(sgn[1], gsl[1], ssl[1]);
+        store(0, sgn[0]);
+        // Every load issued so far completes here (see the row pass).
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        thr_i = next_thr();
+        for (int i = i_lo; i < c1; i += 2) {
+            row_step2(i, std::integral_constant<int, 0>());
+            if (i + 1 < c1)
+                row_step2(i + 1, std::integral_constant<int, 1>());
+        }
+    } else {
     // prologue: rows i_lo and i_lo + 1 stored, far rows i_lo .. i_lo + 2
     // loaded, row i_lo's first operand built
     fetch_q();
@@ -726,6 +770,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(HB 
             row_step(i + 1, std::integral_constant<int, 1>());
         if (i + 2 < c1)
             row_step(i + 2, std::integral_constant<int, 2>());
+    }
     }
 
     // partial[b, chunk, entry, d]: lane = column 32c + n, register r = entry jw + c_row(r, gi)
