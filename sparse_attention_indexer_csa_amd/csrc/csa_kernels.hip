@@ -1259,17 +1259,27 @@ __device__ __forceinline__ bool topk_block_fast(const float *src, int n, int k, 
                 kv[e] = 0u;
         return kv;
     };
-    // pass 2 over the LDS row: count this thread's candidates, place them by
-    // a workgroup prefix sum, then write them (thread order: the sort orders
-    // them)
-    int c = 0;
+    // pass 2 over the LDS row: find this thread's candidates (a bit per key:
+    // its at most 16 blocks of four are 64 keys, the first 32 in hi32, the
+    // rest in lo32, most significant bit first), place them by a workgroup
+    // prefix sum, then write them (thread order: the sort orders them)
+    static_assert(kTopkBlockFastMaxW <= 16 * 4 * NT, "64 keys per thread");
+    uint32_t hi32 = 0u, lo32 = 0u;
 #pragma unroll 4
-    for (int i = t; i < n4; i += NT) {
+    for (int i = t, x = 0; i < n4; i += NT, ++x) {
         const u32x4 kv = block_keys(i);
+        uint32_t &wd = x < 8 ? hi32 : lo32;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            c += (kv[e] - lo <= span) ? 1 : 0;
+            wd = 2u * wd + ((kv[e] - lo <= span) ? 1u : 0u);
     }
+    // left-align the words of a thread with fewer than 16 blocks
+    const int nx = (n4 - t + NT - 1) / NT; // blocks of this thread (t < n4), else <= 0
+    if (nx < 8)
+        hi32 = nx > 0 ? hi32 << (32 - 4 * nx) : 0u;
+    else if (nx > 8 && nx < 16)
+        lo32 = lo32 << (64 - 4 * nx);
+    const int c = __builtin_popcount(hi32) + __builtin_popcount(lo32);
     const int incl = wave_inclusive_sum(c);
     if (lane() == kWave - 1)
         part[wv] = incl;
@@ -1282,20 +1292,20 @@ __device__ __forceinline__ bool topk_block_fast(const float *src, int n, int k, 
     }
     if (m > kBlockCandMax)
         return false;
-    if (c > 0) {
-#pragma unroll 4
-        for (int i = t; i < n4; i += NT) {
-            const u32x4 kv = block_keys(i);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (kv[e] - lo <= span) {
-                    ckey[pos] = kv[e];
-                    cent[pos] = (uint32_t)(4 * i + e);
-                    ++pos;
-                }
-            }
+    // key q (0 .. 63) of this thread is entry 4 (t + NT (q / 4)) + q % 4
+    auto put = [&](uint32_t wd, int q0) {
+        while (wd != 0u) {
+            const int b = __builtin_clz(wd);
+            wd &= ~(0x80000000u >> b);
+            const int q = q0 + b;
+            const uint32_t entry = (uint32_t)(4 * (t + NT * (q >> 2)) + (q & 3));
+            ckey[pos] = row[entry];
+            cent[pos] = entry;
+            ++pos;
         }
-    }
+    };
+    put(hi32, 0);
+    put(lo32, 32);
     __syncthreads();
     // the sort buffer takes the row's place: the LDS holds W >= 8192 keys on
     // this path, at least the 16 KB of 2048 composites (it may cover the

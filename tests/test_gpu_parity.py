@@ -161,6 +161,12 @@ def test_topk_long_rows_exact(dist):
     s2 = np.ascontiguousarray(s[:, :W - 37])
     np.testing.assert_array_equal(to_np(csa.topk(torch.from_numpy(s2).cuda(), 512)), oracle.topk(s2, 512),
                                   err_msg=f"{dist} ragged")
+    # lengths that leave each thread of the in-LDS path 4-5, 8-9 and 15-16
+    # blocks of four keys
+    for w2 in (9001, 16390, 31000):
+        s3 = np.ascontiguousarray(np.concatenate([s, s], axis=1)[:, :w2])
+        np.testing.assert_array_equal(to_np(csa.topk(torch.from_numpy(s3).cuda(), 300)), oracle.topk(s3, 300),
+                                      err_msg=f"{dist} W={w2}")
 
 
 @pytest.mark.parametrize("name,plan", [("c2", "auto"), ("c4", "auto"), ("c5", "auto"), ("c5", "row_tiles")])
