@@ -1079,11 +1079,10 @@ __device__ __forceinline__ uint32_t coarse_threshold(const float *src, int n, in
 // EPT entries: the row is read once into registers (EPT keys per thread, entry
 // e * threads + t in thread t), the coarse histogram gives the bucket of the
 // k-th largest key, the keys above that bucket's lower bound (the candidates,
-// usually a few hundred) are compacted into LDS, and all waves sort them at
-// once with a bitonic network on 64-bit composites (key, ~entry), so that
-// equal keys come out in entry order.  The first k sorted positions are the
-// selection.  Returns false, having written nothing, when there are more
-// than kBlockCandMax candidates.
+// usually a few hundred) are compacted into LDS, and all waves sort them as
+// 64-bit composites (key, ~entry), so that equal keys come out in entry
+// order.  The first k sorted positions are the selection.  Returns false,
+// having written nothing, when there are more than kBlockCandMax candidates.
 constexpr int kBlockCandMax = 2048;
 
 __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int lx)
@@ -1100,94 +1099,127 @@ __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int lx)
     return ((uint64_t)hi << 32) | lo;
 }
 
-// One compare-exchange step between registers r and r + S of each thread
-// (S < PER) in a merge of blocks of `size`.
-template <int PER, int S>
-__device__ __forceinline__ void cex_regs(uint64_t (&v)[PER], int t, int size)
+// The lanes whose index has bit b clear (b a power of two; 64: every lane).
+__device__ __forceinline__ constexpr uint64_t lanes_bit_clear(int b)
 {
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-        if ((r & S) == 0) {
-            const bool desc = ((t * PER + r) & size) == 0;
-            const uint64_t x = v[r], y = v[r + S];
-            v[r] = desc ? max(x, y) : min(x, y);
-            v[r + S] = desc ? min(x, y) : max(x, y);
-        }
-    }
+    return b == 1 ? 0x5555555555555555ull : b == 2 ? 0x3333333333333333ull
+         : b == 4 ? 0x0F0F0F0F0F0F0F0Full : b == 8 ? 0x00FF00FF00FF00FFull
+         : b == 16 ? 0x0000FFFF0000FFFFull : b == 32 ? 0x00000000FFFFFFFFull : ~0ull;
 }
 
-// Descending bitonic sort of N = PER * threads composites, PER per thread at
-// positions t * PER + r.  Partners within a thread are exchanged in
-// registers, within a wave by lane exchanges, across waves through sb
-// (N 64-bit words of LDS).  Fully unrolled: every stride and direction is a
-// constant or a bit of the thread index.
-template <int PER>
-__device__ __forceinline__ void block_bitonic_desc(uint64_t (&v)[PER], uint64_t *sb)
+// Whether to take x for max(x, y) on the lanes of `hi` and min(x, y) on the
+// others: one compare, a scalar operation on the lane masks, no per-lane
+// direction arithmetic.
+__device__ __forceinline__ bool take_first(uint64_t hi, uint64_t x, uint64_t y)
 {
-    constexpr int NT = kTopkBlockWaves * kWave, N = PER * NT;
-    const int t = threadIdx.x;
+    return (x > y) == __builtin_amdgcn_inverse_ballot_w64(hi);
+}
+
+// Descending sort of each wave's own PER * 64 composites (lane l holds
+// wave positions l * PER + r) by a bitonic network in registers and lane
+// exchanges.  In the merge of blocks of SIZE, position p keeps the larger
+// value when bit STRIDE of p equals bit SIZE of p; with p = l * PER + r
+// those are lane bits (or, below PER, bits of r), so each step's direction
+// is a lane mask known at compile time, and SIZE = PER * 64 leaves every
+// wave descending.  Templates, not loops, so that every step is unrolled.
+template <int PER, int SIZE, int STRIDE>
+__device__ __forceinline__ void wave_bitonic_step(uint64_t (&v)[PER])
+{
+    if constexpr (STRIDE < PER) {
 #pragma unroll
-    for (int size = 2; size <= N; size *= 2) {
-#pragma unroll
-        for (int stride = size / 2; stride > 0; stride /= 2) {
-            if (stride < PER) {
-                if constexpr (PER >= 2) {
-                    if (stride == 1)
-                        cex_regs<PER, 1>(v, t, size);
-                }
-                if constexpr (PER >= 4) {
-                    if (stride == 2)
-                        cex_regs<PER, 2>(v, t, size);
-                }
-            } else if (stride < PER * kWave) {
-#pragma unroll
-                for (int r = 0; r < PER; ++r) {
-                    const int p = t * PER + r;
-                    const bool keep_max = ((p & stride) == 0) == ((p & size) == 0);
-                    const uint64_t y = lane_xor_u64(v[r], stride / PER);
-                    v[r] = keep_max ? max(v[r], y) : min(v[r], y);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < PER; ++r)
-                    sb[t * PER + r] = v[r];
-                __syncthreads();
-                uint64_t y[PER];
-#pragma unroll
-                for (int r = 0; r < PER; ++r)
-                    y[r] = sb[(t * PER + r) ^ stride];
-                __syncthreads();
-#pragma unroll
-                for (int r = 0; r < PER; ++r) {
-                    const int p = t * PER + r;
-                    const bool keep_max = ((p & stride) == 0) == ((p & size) == 0);
-                    v[r] = keep_max ? max(v[r], y[r]) : min(v[r], y[r]);
-                }
+        for (int r = 0; r < PER; ++r) {
+            if ((r & STRIDE) == 0) {
+                const uint64_t hi = SIZE < PER ? ((r & SIZE) == 0 ? ~0ull : 0ull) : lanes_bit_clear(SIZE / PER);
+                const uint64_t x = v[r], y = v[r + STRIDE];
+                const bool t = take_first(hi, x, y);
+                v[r] = t ? x : y;
+                v[r + STRIDE] = t ? y : x;
             }
         }
+    } else {
+        constexpr int lx = STRIDE / PER;
+        constexpr uint64_t hi = ~(lanes_bit_clear(lx) ^ lanes_bit_clear(SIZE / PER));
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const uint64_t y = lane_xor_u64(v[r], lx);
+            v[r] = take_first(hi, v[r], y) ? v[r] : y;
+        }
     }
+    if constexpr (STRIDE > 1)
+        wave_bitonic_step<PER, SIZE, STRIDE / 2>(v);
 }
 
-template <int PER>
-__device__ __forceinline__ void block_sort_write(const uint32_t *ckey, const uint32_t *cent, int m, int k,
-                                                 uint64_t *sb, int32_t *out)
+template <int PER, int SIZE = 2>
+__device__ __forceinline__ void wave_bitonic_desc(uint64_t (&v)[PER])
 {
-    const int t = threadIdx.x;
+    wave_bitonic_step<PER, SIZE, SIZE / 2>(v);
+    if constexpr (SIZE < PER * kWave)
+        wave_bitonic_desc<PER, SIZE * 2>(v);
+}
+
+// The m candidates in descending order of (key, -entry), the first k
+// written (entries, -1 past m): each wave sorts PER * 64 of them, the sorted
+// runs go to sb (PER * threads 64-bit words of LDS), and every candidate's
+// final position is the number of composites above it, summed over the runs
+// by a binary search in each.  Composites are distinct (entries are), so the
+// positions are a permutation of 0 .. m-1.
+template <int PER>
+__device__ __forceinline__ void block_merge_write(const uint32_t *ckey, const uint32_t *cent, int m, int k,
+                                                  uint64_t *sb, int32_t *out)
+{
+    constexpr int NW = kTopkBlockWaves, NT = NW * kWave, L = PER * kWave;
+    const int t = threadIdx.x, wv = t / kWave;
     uint64_t v[PER];
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
         const int p = t * PER + r;
         v[r] = p < m ? ((uint64_t)ckey[p] << 32) | (uint32_t)(0xFFFFFFFFu - cent[p]) : 0ull;
     }
-    __syncthreads(); // sb overlaps the candidate arrays
-    block_bitonic_desc<PER>(v, sb);
+    wave_bitonic_desc<PER>(v);
+    __syncthreads(); // sb may overlap the candidate arrays
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-        const int p = t * PER + r;
-        if (p < k)
-            out[p] = p < m ? (int32_t)(0xFFFFFFFFu - (uint32_t)v[r]) : -1;
+    for (int r = 0; r < PER; ++r)
+        sb[t * PER + r] = v[r];
+    __syncthreads();
+    // a wave's candidates sort ahead of its zero padding, so position
+    // t * PER + r holds a candidate exactly when it is below m
+    if (wv * L < m) {
+        int c[NW][PER];
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+            for (int r = 0; r < PER; ++r)
+                c[w][r] = 0;
+        // c = the largest count in [0, L-1] whose last composite is above v
+#pragma unroll
+        for (int st = L / 2; st > 0; st /= 2) {
+            uint64_t a[NW][PER];
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+#pragma unroll
+                for (int r = 0; r < PER; ++r)
+                    a[w][r] = sb[w * L + c[w][r] + st - 1];
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+#pragma unroll
+                for (int r = 0; r < PER; ++r)
+                    c[w][r] += a[w][r] > v[r] ? st : 0;
+        }
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            uint64_t a[NW];
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                a[w] = sb[w * L + c[w][r]];
+            int pos = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                pos += c[w][r] + (a[w] > v[r] ? 1 : 0);
+            if (t * PER + r < m && pos < k)
+                out[pos] = (int32_t)(0xFFFFFFFFu - (uint32_t)v[r]);
+        }
     }
-    for (int p = PER * kTopkBlockWaves * kWave + t; p < k; p += kTopkBlockWaves * kWave)
+    for (int p = m + t; p < k; p += NT)
         out[p] = -1;
 }
 
@@ -1312,11 +1344,11 @@ __device__ __forceinline__ bool topk_block_fast(const float *src, int n, int k, 
     // counters, which are not read again)
     uint64_t *sb = reinterpret_cast<uint64_t *>(row);
     if (m <= NT)
-        block_sort_write<1>(ckey, cent, m, k, sb, out);
+        block_merge_write<1>(ckey, cent, m, k, sb, out);
     else if (m <= 2 * NT)
-        block_sort_write<2>(ckey, cent, m, k, sb, out);
+        block_merge_write<2>(ckey, cent, m, k, sb, out);
     else
-        block_sort_write<4>(ckey, cent, m, k, sb, out);
+        block_merge_write<4>(ckey, cent, m, k, sb, out);
     return true;
 }
 
