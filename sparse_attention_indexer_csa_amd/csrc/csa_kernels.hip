@@ -1099,22 +1099,6 @@ __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int lx)
     return ((uint64_t)hi << 32) | lo;
 }
 
-// The lanes whose index has bit b clear (b a power of two; 64: every lane).
-__device__ __forceinline__ constexpr uint64_t lanes_bit_clear(int b)
-{
-    return b == 1 ? 0x5555555555555555ull : b == 2 ? 0x3333333333333333ull
-         : b == 4 ? 0x0F0F0F0F0F0F0F0Full : b == 8 ? 0x00FF00FF00FF00FFull
-         : b == 16 ? 0x0000FFFF0000FFFFull : b == 32 ? 0x00000000FFFFFFFFull : ~0ull;
-}
-
-// Whether to take x for max(x, y) on the lanes of `hi` and min(x, y) on the
-// others: one compare, a scalar operation on the lane masks, no per-lane
-// direction arithmetic.
-__device__ __forceinline__ bool take_first(uint64_t hi, uint64_t x, uint64_t y)
-{
-    return (x > y) == __builtin_amdgcn_inverse_ballot_w64(hi);
-}
-
 // Descending sort of each wave's own PER * 64 composites (lane l holds
 // wave positions l * PER + r) by a bitonic network in registers and lane
 // exchanges.  In the merge of blocks of SIZE, position p keeps the larger

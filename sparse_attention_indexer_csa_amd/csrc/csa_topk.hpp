@@ -105,6 +105,31 @@ __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v)
     }
 }
 
+// The lanes whose index has bit b clear (b a power of two; 64: every lane).
+__device__ __forceinline__ constexpr uint64_t lanes_bit_clear(int b)
+{
+    return b == 1 ? 0x5555555555555555ull : b == 2 ? 0x3333333333333333ull
+         : b == 4 ? 0x0F0F0F0F0F0F0F0Full : b == 8 ? 0x00FF00FF00FF00FFull
+         : b == 16 ? 0x0000FFFF0000FFFFull : b == 32 ? 0x00000000FFFFFFFFull : ~0ull;
+}
+
+// Whether to take x for max(x, y) on the lanes of `hi` and min(x, y) on the
+// others: one compare, a scalar operation on the lane masks, no per-lane
+// direction arithmetic.
+__device__ __forceinline__ bool take_first(uint64_t hi, uint64_t x, uint64_t y)
+{
+    return (x > y) == __builtin_amdgcn_inverse_ballot_w64(hi);
+}
+
+// All ones in the lanes of m, a lane mask known at compile time, zero in
+// the others.  The mask passes through an empty asm, so the select is made
+// where it is used instead of being hoisted out of enclosing loops.
+__device__ __forceinline__ uint32_t lane_sel(uint64_t m)
+{
+    __asm__ volatile("" : "+s"(m));
+    return __builtin_amdgcn_inverse_ballot_w64(m) ? 0xFFFFFFFFu : 0u;
+}
+
 // The buffer passes below read the keys in batches of kPassBatch chunks of 64
 // (the reads of a batch are in flight together, indexes past the end clamped
 // to the last key) instead of one dependent read per chunk.
@@ -560,13 +585,14 @@ __device__ __forceinline__ void swap_halves(uint32_t &x, uint32_t &y)
     y = sw[1];
 }
 
+// s_first selects the larger value for the first of the two values a lane
+// holds after the swap: in lanes whose LX bit is set that pair is the
+// partner's element r + 1 (first) and this lane's (second), so the results
+// trade places.
 template <int E, int LX>
-__device__ __forceinline__ void cross_stage32_swapped(uint32_t (&v)[E], uint32_t sel, int l)
+__device__ __forceinline__ void cross_stage32_swapped(uint32_t (&v)[E], uint32_t s_first)
 {
     static_assert(E % 2 == 0, "elements are exchanged in pairs");
-    // in lanes whose LX bit is set the pair held is the partner's element
-    // r + 1 (first) and this lane's (second): the results trade places
-    const uint32_t s_first = (l & LX) ? ~sel : sel;
 #pragma unroll
     for (int r = 0; r < E; r += 2)
         swap_halves<LX>(v[r], v[r + 1]);
@@ -585,13 +611,15 @@ template <int E, int SIZE, int STRIDE>
 __device__ __forceinline__ void bitonic32_cross_levels(uint32_t (&v)[E], int l)
 {
     if constexpr (STRIDE >= E && STRIDE >= 1) {
-        const int e = l * E;
-        const bool keep_max = ((e & STRIDE) == 0) == ((e & SIZE) == 0);
-        const uint32_t sel = keep_max ? 0xFFFFFFFFu : 0u;
+        // lane l keeps the larger value when bit STRIDE of l * E equals bit
+        // SIZE of it, i.e. lane bits STRIDE / E and SIZE / E
         constexpr int LX = STRIDE / E;
+        constexpr uint64_t keep = ~(lanes_bit_clear(LX) ^ lanes_bit_clear(SIZE / E));
         if constexpr ((LX == 16 || LX == 32) && E % 2 == 0) {
-            cross_stage32_swapped<E, LX>(v, sel, l);
+            // a lane with bit LX set computes its partner's result first
+            cross_stage32_swapped<E, LX>(v, lane_sel(keep ^ ~lanes_bit_clear(LX)));
         } else {
+            const uint32_t sel = lane_sel(keep);
             // all exchanges first, then the compare-exchanges, so no
             // exchange waits on the result just computed
             uint32_t o[E];
@@ -610,7 +638,8 @@ template <int E, int SIZE>
 __device__ __forceinline__ void bitonic32_in_lane(uint32_t (&v)[E], int l)
 {
     // first element of a pair takes the max when its block sorts descending
-    const uint32_t sel = (((l * E) & SIZE) == 0) ? 0xFFFFFFFFu : 0u;
+    // (bit SIZE of l * E clear: lane bit SIZE / E)
+    const uint32_t sel = SIZE >= E ? lane_sel(lanes_bit_clear(SIZE >= E ? SIZE / E : 1)) : 0u;
 #pragma unroll
     for (int stride = (SIZE / 2 < E / 2 ? SIZE / 2 : E / 2); stride >= 1; stride >>= 1) {
 #pragma unroll
