@@ -68,16 +68,16 @@ FORWARD_SOURCES = ["csa_device.hpp", "csa_kernels.hip", "csa_launch.hpp", "csa_s
 BACKWARD_SOURCES = ["csa_backward.hip", "csa_backward.hpp", "csa_device.hpp", "csa_score.hpp"]
 MEASURED_TRAFFIC = {
     "select": {"sources": FORWARD_SOURCES,
-               "sha": "1aeb4404fc04a283cae3ef6b7e6f44a5e13a794dab2e7b319d5d447471ca5623",
-               "kernels": ["rows3_kernel<128, 2, 2>"], "fetch_bytes": 289501482, "write_bytes": 33554534},
+               "sha": "e0dcde422ec6cd21fc7db4d0469037e6d966be00bc0a10bfc2a8d7c90466779f",
+               "kernels": ["rows3_kernel<128, 2, 2>"], "fetch_bytes": 289702237, "write_bytes": 33554432},
     "decode": {"sources": FORWARD_SOURCES,
-               "sha": "1aeb4404fc04a283cae3ef6b7e6f44a5e13a794dab2e7b319d5d447471ca5623",
-               "kernels": ["stream_kernel<128, 2>", "topk_block_kernel"], "fetch_bytes": 326261647,
+               "sha": "e0dcde422ec6cd21fc7db4d0469037e6d966be00bc0a10bfc2a8d7c90466779f",
+               "kernels": ["stream_kernel<128, 2>", "topk_block_kernel"], "fetch_bytes": 326211944,
                "write_bytes": 5109965},
     "backward": {"sources": BACKWARD_SOURCES,
-                 "sha": "7915e853d7801a745109bfe94b31bc0e61f577c433d8ab4dc3a6649e6ff21db0",
+                 "sha": "424025dd9ebae364fe3f85e8c93efbf7243e623b4174dcf050cdd2434f7c58af",
                  "kernels": ["bwd_rows_kernel<128, 2>", "bwd_keys_kernel<128, 2>", "bwd_reduce_kernel"],
-                 "fetch_bytes": 1493744688, "write_bytes": 882802688},
+                 "fetch_bytes": 1491404161, "write_bytes": 882802688},
 }
 
 DEFAULT_LEGS = "calib,select,score,packed,decode,backward,kl,cpu"
