@@ -1000,12 +1000,11 @@ __device__ __forceinline__ void coarse_add(uint32_t *hist, uint32_t kv)
         atomicAdd(&hist[kv >> (32 - kCoarseBits)], 1u);
 }
 
-// Key below which no key of the row can make its top k: one less than the
-// lower bound of the bucket that holds the k-th largest selectable key
-// (kKeyNegInf when the row has at most k of them), from a complete
-// histogram.  All threads of the workgroup call it; `part` is NW+1 words.
+// The bin holding the k-th largest count of a complete histogram, counting
+// from the top bin down (-1 when the bins hold fewer than k).  All threads
+// of the workgroup call it; `part` is NW+1 words.
 template <int NW>
-__device__ __forceinline__ uint32_t coarse_find(const uint32_t *hist, int k, int *part)
+__device__ __forceinline__ int coarse_find_bin(const uint32_t *hist, int k, int *part)
 {
     constexpr int kThreads = NW * kWave;
     // thread t owns bins kCoarseBins-1-t*P .. (descending), P bins each
@@ -1037,6 +1036,14 @@ __device__ __forceinline__ uint32_t coarse_find(const uint32_t *hist, int k, int
     __syncthreads();
     const int bin = part[NW];
     __syncthreads();
+    return bin;
+}
+
+// Key below which no key of the row can make its top k: one less than the
+// lower bound of the bucket that holds the k-th largest selectable key
+// (kKeyNegInf when the row has fewer than k of them).
+__device__ __forceinline__ uint32_t coarse_tau(int bin)
+{
     return bin <= 0 ? kKeyNegInf : max(((uint32_t)bin << (32 - kCoarseBits)) - 1u, kKeyNegInf);
 }
 
@@ -1072,7 +1079,7 @@ __device__ __forceinline__ uint32_t coarse_threshold(const float *src, int n, in
     for (int j = nv * 4 + threadIdx.x; j < n; j += kThreads)
         coarse_add(hist, score_key(src[j]));
     __syncthreads();
-    return coarse_find<NW>(hist, k, part);
+    return coarse_tau(coarse_find_bin<NW>(hist, k, part));
 }
 
 // Fast path of the long-row top-k for rows of at most kTopkBlockWaves * 64 *
@@ -1262,9 +1269,9 @@ __device__ __forceinline__ bool topk_block_fast(const float *src, int n, int k, 
         coarse_add(hist, kv);
     }
     __syncthreads();
-    // candidates: the keys in (tau, kKeyPosInf]
-    const uint32_t tau = coarse_find<NW>(hist, k, part);
-    const uint32_t lo = tau + 1u, span = kKeyPosInf - lo;
+    // candidates: the keys in [lo, kKeyPosInf]
+    const int bin = coarse_find_bin<NW>(hist, k, part);
+    uint32_t lo = coarse_tau(bin) + 1u;
     // this thread's keys: blocks i = t + NT x of four keys (entries past n
     // read as 0, never a candidate)
     auto block_keys = [&](int i) {
@@ -1278,36 +1285,70 @@ __device__ __forceinline__ bool topk_block_fast(const float *src, int n, int k, 
     // pass 2 over the LDS row: find this thread's candidates (a bit per key:
     // its at most 16 blocks of four are 64 keys, the first 32 in hi32, the
     // rest in lo32, most significant bit first), place them by a workgroup
-    // prefix sum, then write them (thread order: the sort orders them)
+    // prefix sum (pos: this thread's first place, m: all candidates)
     static_assert(kTopkBlockFastMaxW <= 16 * 4 * NT, "64 keys per thread");
-    uint32_t hi32 = 0u, lo32 = 0u;
+    uint32_t hi32, lo32;
+    int pos, m;
+    auto mark = [&]() {
+        const uint32_t span = kKeyPosInf - lo;
+        hi32 = 0u;
+        lo32 = 0u;
 #pragma unroll 4
-    for (int i = t, x = 0; i < n4; i += NT, ++x) {
-        const u32x4 kv = block_keys(i);
-        uint32_t &wd = x < 8 ? hi32 : lo32;
+        for (int i = t, x = 0; i < n4; i += NT, ++x) {
+            const u32x4 kv = block_keys(i);
+            uint32_t &wd = x < 8 ? hi32 : lo32;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            wd = 2u * wd + ((kv[e] - lo <= span) ? 1u : 0u);
-    }
-    // left-align the words of a thread with fewer than 16 blocks
-    const int nx = (n4 - t + NT - 1) / NT; // blocks of this thread (t < n4), else <= 0
-    if (nx < 8)
-        hi32 = nx > 0 ? hi32 << (32 - 4 * nx) : 0u;
-    else if (nx > 8 && nx < 16)
-        lo32 = lo32 << (64 - 4 * nx);
-    const int c = __builtin_popcount(hi32) + __builtin_popcount(lo32);
-    const int incl = wave_inclusive_sum(c);
-    if (lane() == kWave - 1)
-        part[wv] = incl;
-    __syncthreads();
-    int pos = incl - c, m = 0;
+            for (int e = 0; e < 4; ++e)
+                wd = 2u * wd + ((kv[e] - lo <= span) ? 1u : 0u);
+        }
+        // left-align the words of a thread with fewer than 16 blocks
+        const int nx = (n4 - t + NT - 1) / NT; // blocks of this thread (t < n4), else <= 0
+        if (nx < 8)
+            hi32 = nx > 0 ? hi32 << (32 - 4 * nx) : 0u;
+        else if (nx > 8 && nx < 16)
+            lo32 = lo32 << (64 - 4 * nx);
+        const int c = __builtin_popcount(hi32) + __builtin_popcount(lo32);
+        const int incl = wave_inclusive_sum(c);
+        if (lane() == kWave - 1)
+            part[wv] = incl;
+        __syncthreads();
+        pos = incl - c;
+        m = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        pos += w < wv ? part[w] : 0;
-        m += part[w];
+        for (int w = 0; w < NW; ++w) {
+            pos += w < wv ? part[w] : 0;
+            m += part[w];
+        }
+    };
+    mark();
+    if (m > kBlockCandMax) {
+        // The k-th largest key's bucket holds too many keys (ties, or scores
+        // packed closely): histogram that bucket's keys by their next
+        // kCoarseBits bits and move the threshold to the sub-bucket holding
+        // the k-th largest key.
+        if (bin < 0)
+            return false; // fewer than k selectable keys: every one is a candidate
+        const int above = m - (int)hist[bin];
+        __syncthreads(); // hist[bin] and part read by every thread
+        coarse_clear<NW>(hist);
+        __syncthreads();
+        constexpr int kSub = 32 - 2 * kCoarseBits;
+        for (int i = t; i < n4; i += NT) {
+            const u32x4 kv = block_keys(i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (key_selectable(kv[e]) && (int)(kv[e] >> (32 - kCoarseBits)) == bin)
+                    atomicAdd(&hist[(kv[e] >> kSub) & (kCoarseBins - 1)], 1u);
+        }
+        __syncthreads();
+        const int sub = coarse_find_bin<NW>(hist, k - above, part);
+        if (sub < 0)
+            return false; // not reached: the bucket holds at least k - above keys
+        lo = ((uint32_t)bin << (32 - kCoarseBits)) | ((uint32_t)sub << kSub);
+        mark();
+        if (m > kBlockCandMax)
+            return false;
     }
-    if (m > kBlockCandMax)
-        return false;
     // key q (0 .. 63) of this thread is entry 4 (t + NT (q / 4)) + q % 4
     auto put = [&](uint32_t wd, int q0) {
         while (wd != 0u) {
