@@ -236,7 +236,9 @@ csa_status launched(hipError_t e, const char *what)
 }
 
 // Top-k over rows of length up to W: the workgroup-per-row kernel for long
-// rows when its LDS fits, else one wave per row.
+// rows when its LDS fits, else one wave per row.  When only the in-LDS part
+// of the workgroup kernel fits (large k), it runs first and one wave per row
+// then takes the rows it could not.
 csa_status launch_topk_rows(csa::KernelArgs &a, hipStream_t s)
 {
     DeviceInfo d;
@@ -245,11 +247,19 @@ csa_status launch_topk_rows(csa::KernelArgs &a, hipStream_t s)
         return st;
     const int lim = d.lds;
     size_t block_lds = csa::topk_block_lds_bytes(a.cap, a.top_k, a.W);
+    a.redo = 0;
     if (a.W >= csa::kTopkBlockMinLen && block_lds <= (size_t)lim)
         return launched(csa::launch_topk_block(a, block_lds, s), "top-k");
     size_t lds = csa::topk_lds_bytes(a.cap);
     if (lds > (size_t)lim)
         return fail(CSA_ERR_UNSUPPORTED, "top-k needs %zu bytes of LDS per workgroup, device allows %d", lds, lim);
+    const size_t fast_lds = csa::topk_block_fast_only_lds_bytes(a.top_k, a.W);
+    if (fast_lds != 0 && fast_lds <= (size_t)lim) {
+        a.redo = 1;
+        st = launched(csa::launch_topk_block(a, fast_lds, s), "top-k");
+        if (st != CSA_OK)
+            return st;
+    }
     return launched(csa::launch_topk(a, lds, s), "top-k");
 }
 

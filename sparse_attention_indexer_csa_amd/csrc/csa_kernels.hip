@@ -964,6 +964,8 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(const KernelAr
     const int64_t row = (int64_t)blockIdx.x * kTopkWaves + wv;
     if (row >= a.rows)
         return;
+    if (a.redo && a.idx[row * a.top_k] != kTopkRedo)
+        return; // the workgroup-per-row kernel selected this row
     const int n = row_length(a, row);
     unsigned char *base = smem + (size_t)wv * (1024 + (size_t)a.cap * 8);
     uint32_t *hist = reinterpret_cast<uint32_t *>(base);
@@ -1401,6 +1403,11 @@ __global__ __launch_bounds__(kTopkBlockWaves * kWave) void topk_block_kernel(con
     if (a.W <= kTopkBlockFastMaxW) {
         if (topk_block_fast(src, n, a.top_k, smem, a.idx + row * a.top_k))
             return;
+        if (a.redo) { // the LDS holds the in-LDS path only: leave the row to topk_kernel
+            if (threadIdx.x == 0)
+                a.idx[row * a.top_k] = kTopkRedo;
+            return;
+        }
         __syncthreads(); // the streaming path below reuses the same LDS
     }
     TopKRow<uint32_t> tk;
@@ -1519,6 +1526,15 @@ size_t rows_lds_bytes(int D, int HB, int mode, int cap)
 }
 
 size_t topk_lds_bytes(int cap) { return (size_t)kTopkWaves * (1024 + (size_t)cap * 8); }
+
+size_t topk_block_fast_only_lds_bytes(int top_k, int W)
+{
+    // k close to the candidate room leaves the in-LDS path too little slack
+    // to succeed on any row
+    if (W < kTopkBlockMinLen || W > kTopkBlockFastMaxW || top_k > kBlockCandMax - kBlockCandMax / 16)
+        return 0;
+    return topk_block_fast_lds_bytes(W);
+}
 
 size_t topk_block_lds_bytes(int cap, int top_k, int W)
 {

@@ -29,6 +29,7 @@ struct KernelArgs {
     int32_t n_chunks;     // split plan: workgroups per row
     int32_t full_rows;    // split plan: write every score of the row (-inf past the visible prefix)
     int32_t limit_rows;   // top-k kernel: rows end at their visible prefix (q_offset, m)
+    int32_t redo;         // top-k kernels in two passes: see kTopkRedo
     float scale;
 };
 
@@ -78,6 +79,15 @@ constexpr int kRowTilesMaxW = 65536;
 size_t rows_lds_bytes(int D, int HB, int mode, int cap);
 size_t topk_lds_bytes(int cap);
 size_t topk_block_lds_bytes(int cap, int top_k, int W);
+// LDS of the workgroup-per-row kernel without its streaming fallback (the
+// in-LDS path alone), or 0 when that path cannot take rows of W entries or
+// would rarely succeed for k (k above 1920).
+size_t topk_block_fast_only_lds_bytes(int top_k, int W);
+// Two-pass top-k, for k whose streaming fallback does not fit in one
+// workgroup's LDS: with redo set, topk_block_kernel writes a row that its
+// in-LDS path cannot take as kTopkRedo in the row's first output, and
+// topk_kernel then selects only the rows so marked.
+constexpr int32_t kTopkRedo = -2;
 
 // Each returns hipSuccess or the launch error; nothing is synchronised.
 hipError_t launch_rows(int D, int HB, int mode, const KernelArgs &a, size_t lds, hipStream_t s);
