@@ -68,16 +68,16 @@ FORWARD_SOURCES = ["csa_device.hpp", "csa_kernels.hip", "csa_launch.hpp", "csa_s
 BACKWARD_SOURCES = ["csa_backward.hip", "csa_backward.hpp", "csa_device.hpp", "csa_score.hpp"]
 MEASURED_TRAFFIC = {
     "select": {"sources": FORWARD_SOURCES,
-               "sha": "e0dcde422ec6cd21fc7db4d0469037e6d966be00bc0a10bfc2a8d7c90466779f",
-               "kernels": ["rows3_kernel<128, 2, 2>"], "fetch_bytes": 289702237, "write_bytes": 33554432},
+               "sha": "350cc1929d13630e14ef5def11d5f4a8e6721c2190b2a3c7a8343ca8389e6e77",
+               "kernels": ["rows3_kernel<128, 2, 2>"], "fetch_bytes": 289589063, "write_bytes": 33554464},
     "decode": {"sources": FORWARD_SOURCES,
-               "sha": "e0dcde422ec6cd21fc7db4d0469037e6d966be00bc0a10bfc2a8d7c90466779f",
-               "kernels": ["stream_kernel<128, 2>", "topk_block_kernel"], "fetch_bytes": 326211944,
-               "write_bytes": 5109965},
+               "sha": "350cc1929d13630e14ef5def11d5f4a8e6721c2190b2a3c7a8343ca8389e6e77",
+               "kernels": ["stream_kernel<128, 2>", "topk_block_kernel"], "fetch_bytes": 326233731,
+               "write_bytes": 5109952},
     "backward": {"sources": BACKWARD_SOURCES,
                  "sha": "424025dd9ebae364fe3f85e8c93efbf7243e623b4174dcf050cdd2434f7c58af",
                  "kernels": ["bwd_rows_kernel<128, 2>", "bwd_keys_kernel<128, 2>", "bwd_reduce_kernel"],
-                 "fetch_bytes": 1491404161, "write_bytes": 882802688},
+                 "fetch_bytes": 1503964918, "write_bytes": 882802688},
 }
 
 DEFAULT_LEGS = "calib,select,score,packed,decode,backward,kl,cpu"
