@@ -169,6 +169,24 @@ def test_topk_long_rows_exact(dist):
                                       err_msg=f"{dist} W={w2}")
 
 
+def test_topk_large_k_two_pass():
+    """k whose streaming fallback does not fit one workgroup's LDS: the
+    in-LDS path takes the rows it can, marks the others, and one wave per row
+    selects those (tied rows); rows packed into one coarse bucket go through
+    the split of that bucket by the next key bits."""
+    rng = np.random.default_rng(17)
+    W = 32768
+    s = rng.standard_normal((7, W)).astype(np.float32)
+    s[1] = rng.integers(-2, 3, size=W).astype(np.float32)      # ties: handed over
+    s[2] = (1.0 + rng.random(W) * 2.0 ** -10).astype(np.float32)  # one coarse bucket
+    s[3, 5000:] = -np.inf
+    s[4, :] = -np.inf                                          # nothing selectable
+    s[5, ::3] = np.nan
+    for k in (512, 1700, 1920, 1921):
+        np.testing.assert_array_equal(to_np(csa.topk(torch.from_numpy(s).cuda(), k)), oracle.topk(s, k),
+                                      err_msg=f"k={k}")
+
+
 @pytest.mark.parametrize("name,plan", [("c2", "auto"), ("c4", "auto"), ("c5", "auto"), ("c5", "row_tiles")])
 def test_fused_select_equals_topk_of_scores(name, plan):
     P = make_config(name)
