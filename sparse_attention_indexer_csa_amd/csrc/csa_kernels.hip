@@ -1084,14 +1084,15 @@ __device__ __forceinline__ uint32_t coarse_threshold(const float *src, int n, in
     return coarse_tau(coarse_find_bin<NW>(hist, k, part));
 }
 
-// Fast path of the long-row top-k for rows of at most kTopkBlockWaves * 64 *
-// EPT entries: the row is read once into registers (EPT keys per thread, entry
-// e * threads + t in thread t), the coarse histogram gives the bucket of the
-// k-th largest key, the keys above that bucket's lower bound (the candidates,
-// usually a few hundred) are compacted into LDS, and all waves sort them as
-// 64-bit composites (key, ~entry), so that equal keys come out in entry
-// order.  The first k sorted positions are the selection.  Returns false,
-// having written nothing, when there are more than kBlockCandMax candidates.
+// Fast path of the long-row top-k for rows of at most kTopkBlockFastMaxW
+// entries: the row is read once from global memory into LDS as keys, with the
+// coarse histogram built on the way; its bucket of the k-th largest key (split
+// once more by the next key bits when it holds too many) bounds the
+// candidates, usually a few hundred, which are compacted into LDS; the waves
+// sort them as 64-bit composites (key, ~entry), so that equal keys come out
+// in entry order, and the first k sorted positions are the selection.
+// Returns false, having written nothing, when there are more than
+// kBlockCandMax candidates.
 constexpr int kBlockCandMax = 2048;
 
 __device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int lx)
