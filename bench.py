@@ -68,10 +68,10 @@ FORWARD_SOURCES = ["csa_device.hpp", "csa_kernels.hip", "csa_launch.hpp", "csa_s
 BACKWARD_SOURCES = ["csa_backward.hip", "csa_backward.hpp", "csa_device.hpp", "csa_score.hpp"]
 MEASURED_TRAFFIC = {
     "select": {"sources": FORWARD_SOURCES,
-               "sha": "b3caf159fcbbcac9612d29be98259f16d7f6d4029350446de7e19db2bc3dd382",
+               "sha": "d2d37f996557ed10960dce85db9b54223ada86546d92d7ac68eab3c92e6de076",
                "kernels": ["rows3_kernel<128, 2, 2>"], "fetch_bytes": 289589063, "write_bytes": 33554464},
     "decode": {"sources": FORWARD_SOURCES,
-               "sha": "b3caf159fcbbcac9612d29be98259f16d7f6d4029350446de7e19db2bc3dd382",
+               "sha": "d2d37f996557ed10960dce85db9b54223ada86546d92d7ac68eab3c92e6de076",
                "kernels": ["stream_kernel<128, 2>", "topk_block_kernel"], "fetch_bytes": 326233731,
                "write_bytes": 5109952},
     "backward": {"sources": BACKWARD_SOURCES,

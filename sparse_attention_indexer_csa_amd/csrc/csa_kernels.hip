@@ -978,13 +978,14 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void topk_kernel(const KernelAr
 }
 
 // ---------------------------------------------------------------------------
-// Row top-k for long rows: one workgroup per row.  A first pass builds a
-// histogram of the row's keys by their top kCoarseBits bits and finds the
-// bucket holding the k-th largest key: every key below that bucket is beaten
-// by at least k others, so the waves start with tau just below it and their
-// buffers only ever see the few keys at or above it.  Wave w then streams
-// the w-th contiguous segment into its own buffer, and the waves select
-// jointly.
+// Row top-k for long rows: one workgroup per row.  Rows whose keys fit in
+// LDS take the fast path below (topk_block_fast); the others, and the rows
+// it declines, take the streaming path: a first pass builds a histogram of
+// the row's keys by their top kCoarseBits bits and finds the bucket holding
+// the k-th largest key: every key below that bucket is beaten by at least k
+// others, so the waves start with tau just below it and their buffers only
+// ever see the few keys at or above it.  Wave w then streams the w-th
+// contiguous segment into its own buffer, and the waves select jointly.
 // ---------------------------------------------------------------------------
 constexpr int kCoarseBits = 12;
 constexpr int kCoarseBins = 1 << kCoarseBits;

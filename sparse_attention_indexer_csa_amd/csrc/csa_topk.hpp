@@ -3,13 +3,17 @@
 // Wave level (TopKRow): one wave owns a row and receives its (key, entry)
 // pairs 64 at a time in increasing entry order.  It keeps a candidate buffer
 // of `cap` pairs in LDS and a threshold tau: a pair may enter only if its key
-// is > tau.  When the buffer would overflow, a radix select finds T, the k-th
-// largest key in the buffer, and an order-preserving compaction keeps every
-// key > T plus the earliest keys == T, k pairs in all; tau becomes T.  A later
-// pair with key <= T can never make the top k: k kept pairs beat it (larger
-// key, or equal key and lower entry).  At the end the same select leaves
-// exactly min(k, count) pairs, which a bitonic sort orders by (key
-// descending, entry ascending).
+// is > tau.  When the buffer would overflow, one histogram over the buffer's
+// key range finds the bucket of the k-th largest key, an order-preserving
+// compaction keeps every key at or above that bucket (at least k pairs), and
+// tau becomes the bucket's lower bound minus one; if that would free too
+// little room, a radix select finds T, the k-th largest key in the buffer,
+// and the compaction keeps every key > T plus the earliest keys == T, k pairs
+// in all, with tau = T.  A later pair with key <= tau can never make the top
+// k: k kept pairs beat it (larger key, or equal key and lower entry).  At the
+// end a final select (the radix select, or its version over registers in the
+// row kernels) leaves exactly min(k, count) pairs, which a bitonic sort
+// orders by (key descending, entry ascending).
 //
 // Block level (block_select_sort): several waves that each hold a candidate
 // buffer for a contiguous segment of one row (segments in increasing entry
