@@ -799,15 +799,31 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdArgs a)
     const int b = (int)(v / per_b);
     const int64_t e = (v % per_b) * 4; // element within [W, D]
     const int jtile0 = (int)(e / D) / kBwdKeyTile * kBwdKeyTile;
+    // the partials of kBatch chunks are read together (one memory latency
+    // per batch, not per chunk) and added in chunk order
+    constexpr int kBatch = 8;
+    const int64_t off = row_offset(a, b); // (chunk_live, with the offset read once)
     float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int c = 0; c < a.n_chunks; ++c) {
-        if (!chunk_live(a, b, c, jtile0))
-            continue;
-        const float4 p = *reinterpret_cast<const float4 *>(a.part + (((int64_t)b * a.n_chunks + c) * a.W) * D + e);
-        s.x += p.x;
-        s.y += p.y;
-        s.z += p.z;
-        s.w += p.w;
+    for (int c0 = 0; c0 < a.n_chunks; c0 += kBatch) {
+        float4 p[kBatch];
+        bool live[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int c = c0 + u;
+            const int last = min((c + 1) * kBwdChunkRows, a.S) - 1;
+            live[u] = c < a.n_chunks && visible_entries(off + last, a.m, a.W) > jtile0;
+            p[u] = live[u] ? *reinterpret_cast<const float4 *>(a.part + (((int64_t)b * a.n_chunks + c) * a.W) * D + e)
+                           : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (live[u]) {
+                s.x += p[u].x;
+                s.y += p[u].y;
+                s.z += p[u].z;
+                s.w += p[u].w;
+            }
+        }
     }
     float4 o = make_float4(a.scale * s.x, a.scale * s.y, a.scale * s.z, a.scale * s.w);
     *reinterpret_cast<float4 *>(a.dk + (int64_t)b * a.W * D + e) = o;
