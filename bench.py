@@ -69,15 +69,15 @@ BACKWARD_SOURCES = ["csa_backward.hip", "csa_backward.hpp", "csa_device.hpp", "c
 MEASURED_TRAFFIC = {
     "select": {"sources": FORWARD_SOURCES,
                "sha": "d2d37f996557ed10960dce85db9b54223ada86546d92d7ac68eab3c92e6de076",
-               "kernels": ["rows3_kernel<128, 2, 2>"], "fetch_bytes": 289589063, "write_bytes": 33554464},
+               "kernels": ["rows3_kernel<128, 2, 2>"], "fetch_bytes": 289429128, "write_bytes": 33554432},
     "decode": {"sources": FORWARD_SOURCES,
                "sha": "d2d37f996557ed10960dce85db9b54223ada86546d92d7ac68eab3c92e6de076",
-               "kernels": ["stream_kernel<128, 2>", "topk_block_kernel"], "fetch_bytes": 326233731,
+               "kernels": ["stream_kernel<128, 2>", "topk_block_kernel"], "fetch_bytes": 326239355,
                "write_bytes": 5109952},
     "backward": {"sources": BACKWARD_SOURCES,
-                 "sha": "424025dd9ebae364fe3f85e8c93efbf7243e623b4174dcf050cdd2434f7c58af",
+                 "sha": "a7ca52bcf26cfb3fd8efe55801257ab8ae3597f7878ce3a36c165df0bb12e886",
                  "kernels": ["bwd_rows_kernel<128, 2>", "bwd_keys_kernel<128, 2>", "bwd_reduce_kernel"],
-                 "fetch_bytes": 1503964918, "write_bytes": 882802688},
+                 "fetch_bytes": 1499413736, "write_bytes": 882802688},
 }
 
 DEFAULT_LEGS = "calib,select,score,packed,decode,backward,kl,cpu"
